@@ -1,0 +1,13 @@
+"""CPU oracle for the MoE token dispatch / grouped expert FFN / combine path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this package: only the test suite, the graft entry's ``smoke()`` check
+and the bench's ``cpu_baseline`` leg use it. It shares no code with the HIP
+library and imports nothing from it.
+
+Everything is plain NumPy in float64, written to be checked by eye against
+the layer's definition; see ``oracle.moe`` for the functions and the passages
+each one follows.
+"""
+from .moe import *  # noqa: F401,F403
+from .moe import __all__  # noqa: F401
