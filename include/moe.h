@@ -1,0 +1,252 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE dispatch / grouped-FFN / combine
+ * library.
+ *
+ * One MoE expert layer, forward and backward, on one GPU: top-k softmax
+ * routing, dropless token dispatch into expert-contiguous rows, a grouped
+ * SwiGLU expert FFN, and the weighted combine back to source order.
+ *
+ * The pages this follows name the hot path as "EP token dispatch" plus
+ * "grouped expert compute" ("Add MoE expert parallel training runtime",
+ * Major changes), and require that uneven or empty work neither
+ * desynchronises nor crashes it, that callers never pad, that outputs come
+ * back in full source order and that gradients accumulate ("Support combined
+ * expert and data parallelism in TrainerRank", Desired behavior and
+ * Acceptance). Unsupported configurations fail loudly and up front, and every
+ * argument is validated before any is used (same page, Current behavior;
+ * review note on "Add MoE expert parallel training runtime").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor is a device pointer to contiguous row-major memory, owned
+ *    by the caller. The library never allocates, frees or keeps device
+ *    memory; scratch memory is passed in as a workspace whose size
+ *    moe_workspace_size() reports.
+ *  - "s" below is the layer dtype: MOE_DTYPE_BF16 (bf16 storage, fp32
+ *    accumulation, results rounded to nearest-even once) or MOE_DTYPE_F32.
+ *    Routing tensors (logits, weights, their gradients) and weight gradients
+ *    are always fp32; index tensors are int32.
+ *  - Weights use the [out, in] convention: w_gu is [E, 2F, d] with the gate
+ *    projection in rows [0, F) and the up projection in rows [F, 2F) of each
+ *    expert; w_down is [E, d, F].
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *    stream). The host never waits for the device and never reads device
+ *    data; per-expert row counts stay on the device.
+ *  - T == 0 (an empty microbatch) returns MOE_OK, launches nothing and writes
+ *    nothing; NULL is then accepted for every tensor.
+ *  - Validation happens on the host before the first launch. A NULL pointer
+ *    that must be read or written, a pointer not aligned to 16 bytes, a
+ *    shape outside the supported matrix or a short workspace is reported
+ *    with a status code and nothing is launched. No C++ exception crosses
+ *    this interface.
+ *  - Supported matrix: T >= 0, 1 <= k <= E <= 256, k <= 16, d and F
+ *    positive multiples of 64, d <= 65536, F <= 65536, T*k < 2^31,
+ *    dtype bf16 or fp32. Anything else returns MOE_ERR_UNSUPPORTED.
+ *  - Calls that overlap on one stream are ordered; calls on different
+ *    streams that share buffers race, as with any HIP kernel.
+ *
+ * Numbering used in the comments: R = T*k routed rows; M_e = counts[e].
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* NULL where data is needed, negative size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2,      /* outside the supported matrix above */
+  MOE_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required */
+  MOE_ERR_MISALIGNED = 4,       /* a tensor pointer not 16-byte aligned */
+  MOE_ERR_HIP = 5               /* a HIP launch failed; see moe_last_error() */
+} moe_status;
+
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+/* Renormalise the k selected weights so that they sum to one. Without it the
+ * weights are the full-softmax probabilities of the selected experts. */
+enum { MOE_FLAG_RENORM = 1u };
+
+typedef struct moe_shape {
+  int64_t T;      /* tokens in this microbatch (>= 0) */
+  int32_t d;      /* hidden size */
+  int32_t E;      /* experts held by this GPU */
+  int32_t k;      /* experts per token */
+  int32_t F;      /* SwiGLU hidden size of one expert */
+  int32_t dtype;  /* MOE_DTYPE_F32 or MOE_DTYPE_BF16 */
+  uint32_t flags; /* MOE_FLAG_* */
+} moe_shape;
+
+/* Opaque stream handle: a hipStream_t, or NULL for the default stream. */
+typedef void *moe_stream_t;
+
+/*
+ * Workspace sizes in bytes for a shape: route_ws serves moe_route and
+ * moe_route_bwd, gemm_fwd_ws serves moe_grouped_gemm_fwd and gemm_bwd_ws
+ * serves moe_grouped_gemm_bwd. A workspace sized for some T serves every
+ * smaller T of the same (d, E, k, F, dtype), so one buffer sized for the
+ * largest microbatch can be reused across microbatches of any size
+ * ("live-graph/buffer-capacity transitions", Support combined expert and
+ * data parallelism in TrainerRank, Acceptance). Any output pointer may be
+ * NULL. Pure host function.
+ */
+moe_status moe_workspace_size(const moe_shape *shape, size_t *route_ws, size_t *gemm_fwd_ws,
+                              size_t *gemm_bwd_ws);
+
+/*
+ * Routing and dispatch tables (the routing half of "EP token dispatch").
+ *
+ * If w_router is non-NULL the logits are computed first,
+ *   logits[t,e] = <x[t], w_router[e]> + bias[e]   (fp32 accumulation),
+ * with x [T,d] s, w_router [E,d] s and bias [E] fp32 (NULL means zero), and
+ * written to `logits`. Otherwise x, w_router and bias must be NULL and
+ * `logits` [T,E] fp32 is read.
+ *
+ * Then, per token: topk_idx[t,:] [T,k] int32 holds the k largest logits in
+ * descending order, equal logits going to the lower expert id (NaN ranks
+ * below -inf; -0.0 equals +0.0); topk_w[t,j] [T,k] fp32 is
+ * softmax(logits[t,:])[topk_idx[t,j]], divided by the sum over j when
+ * MOE_FLAG_RENORM is set. Every token needs at least one finite logit.
+ *
+ * Dispatch tables: counts[e] [E] int32 rows per expert; offsets [E+1] int32
+ * the exclusive prefix sum (offsets[E] = R); row_of_slot[t,j] [T,k] int32 the
+ * row of the expert-contiguous buffers that receives slot (t,j); and
+ * src_of_row[r] [R] int32 = t*k+j, its inverse. Rows of one expert follow
+ * ascending source token (a stable counting sort); the order is decided
+ * without atomics, so the tables are identical run to run.
+ *
+ * ws: route workspace of at least route_ws bytes.
+ */
+moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                     float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                     int32_t *offsets, int32_t *row_of_slot, int32_t *src_of_row, void *ws,
+                     size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Token dispatch (the data-moving half of "EP token dispatch"):
+ *   x_perm[row_of_slot[t,j]] = x[t]     x [T,d] s -> x_perm [R,d] s.
+ * Each source row is read once and written k times. No padding rows exist:
+ * the buffers hold exactly R rows.
+ */
+moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *row_of_slot,
+                       void *x_perm, moe_stream_t stream);
+
+/*
+ * Grouped SwiGLU expert FFN ("grouped expert compute"), expert by expert over
+ * the rows [offsets[e], offsets[e+1]) of x_perm:
+ *   h = X_e W_gu[e]^T         [R,2F] s   (saved for the backward)
+ *   a = silu(h[:, :F]) * h[:, F:]  [R,F] s   (saved)
+ *   y = a W_down[e]^T         [R,d] s   (unweighted expert output)
+ * silu(z) = z / (1 + exp(-z)). The gate/up products feed the SwiGLU in fp32
+ * before h and a are rounded. An expert with no rows costs nothing: tiles
+ * are laid out on the device from `offsets`, which the host never reads.
+ * ws: at least gemm_fwd_ws bytes (may be NULL when that size is 0).
+ */
+moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, const void *w_gu,
+                                const void *w_down, const int32_t *offsets, void *h, void *a,
+                                void *y, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Weighted combine back to full source order:
+ *   out[t] = sum_{j<k} topk_w[t,j] * y[row_of_slot[t,j]]    out [T,d] s,
+ * summed in fp32 in increasing j and rounded once.
+ */
+moe_status moe_unpermute_combine(const moe_shape *shape, const void *y, const float *topk_w,
+                                 const int32_t *row_of_slot, void *out, moe_stream_t stream);
+
+/*
+ * Backward of the combine:
+ *   dy[row_of_slot[t,j]] = topk_w[t,j] * dout[t]     dy [R,d] s
+ *   dtopk_w[t,j] = <dout[t], y[row_of_slot[t,j]]>   dtopk_w [T,k] fp32
+ */
+moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dout, const void *y,
+                                     const float *topk_w, const int32_t *row_of_slot, void *dy,
+                                     float *dtopk_w, moe_stream_t stream);
+
+/*
+ * Backward of the routing weights. Selection is piecewise constant, so only
+ * the weights carry gradient. With g = dtopk_w and p = softmax(logits[t,:]):
+ *   no renorm: dlogits[t,m] = p_m * (G_m - sum_j topk_w[t,j] g[t,j]),
+ *              G_m = g[t,j] if m == topk_idx[t,j] for some j, else 0;
+ *   renorm:    dlogits[t,topk_idx[t,j]] = topk_w[t,j] (g[t,j] - sum_j' topk_w g),
+ *              zero for unselected experts.
+ * dlogits [T,E] fp32 is overwritten.
+ *
+ * If w_router is non-NULL (the logits came from the router inside
+ * moe_route), x [T,d] s and w_router [E,d] s are read and
+ *   dx_router = dlogits w_router   [T,d] fp32 (overwritten),
+ *   dw_router += dlogits^T x       [E,d] fp32 (accumulated; zero it once),
+ * both required; otherwise x, dx_router and dw_router must be NULL. The
+ * router weight gradient is reduced in a fixed order (no atomics).
+ * ws: route workspace of at least route_ws bytes.
+ */
+moe_status moe_route_bwd(const moe_shape *shape, const float *dtopk_w, const float *logits,
+                         const int32_t *topk_idx, const float *topk_w, const void *x,
+                         const void *w_router, float *dlogits, float *dx_router, float *dw_router,
+                         void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Backward of the grouped SwiGLU FFN, expert by expert:
+ *   dA      = dY_e W_down[e]
+ *   dH_gate = dA * h_up * sig(h_gate) * (1 + h_gate (1 - sig(h_gate)))
+ *   dH_up   = dA * silu(h_gate)                   (dH kept in ws, dtype s)
+ *   dx_perm = dH W_gu[e]                          [R,d] s   (overwritten)
+ *   dw_down[e] += dY_e^T a_e                      [E,d,F] fp32
+ *   dw_gu[e]   += dH^T X_e                        [E,2F,d] fp32
+ * The weight gradients accumulate across calls (gradient accumulation across
+ * microbatches and repeated forwards: Support pipeline parallelism in
+ * TrainerRank without exposing stage scheduling to callers, Acceptance); the
+ * caller zeroes them once. An expert with no rows leaves its dw slices
+ * bit-identical. Each dw element is reduced by one workgroup in a fixed
+ * order, so results are identical run to run.
+ * ws: at least gemm_bwd_ws bytes.
+ */
+moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const void *x_perm,
+                                const void *h, const void *a, const void *w_gu, const void *w_down,
+                                const int32_t *offsets, void *dx_perm, float *dw_gu, float *dw_down,
+                                void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Backward of the dispatch:
+ *   dx[t] = sum_j dx_perm[row_of_slot[t,j]] (+ dx_extra[t])    dx [T,d] s,
+ * summed in fp32 and rounded once. dx_extra [T,d] fp32 (the router's
+ * contribution from moe_route_bwd) may be NULL.
+ */
+moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const int32_t *row_of_slot,
+                           const float *dx_extra, void *dx, moe_stream_t stream);
+
+/* Static English text for a status code. */
+const char *moe_status_string(moe_status status);
+
+/* Detail of the last error reported on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/*
+ * Per-kernel timing with HIP events, for measurement. When enabled, every
+ * kernel the library launches is bracketed by two events recorded on the
+ * launch stream; moe_profiler_read() waits for them and returns, per kernel
+ * name, the number of launches and the summed elapsed milliseconds since the
+ * last moe_profiler_reset(). Host-side state, not thread-safe; meant for a
+ * single measuring thread. Disabled by default.
+ */
+moe_status moe_profiler_enable(int on);
+moe_status moe_profiler_reset(void);
+/* Number of distinct kernel names recorded so far. */
+int moe_profiler_count(void);
+/* Entry i: name (static string), launches, total ms. Blocks until the events
+ * of that entry have completed. */
+moe_status moe_profiler_read(int i, const char **name, int64_t *launches, double *total_ms);
+
+/* Library version string. */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,217 @@
+"""ctypes binding of ``libmoe_mi355x.so`` (see ``include/moe.h``).
+
+Argument marshalling only: every function here has the name of the C entry
+point it calls, turns tensors into device pointers and the current torch
+stream into a ``hipStream_t``, and raises :class:`MoeError` on a non-OK
+status. No step of the layer is computed in Python, and there is no CPU
+fallback: if the library has not been built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_MISALIGNED = 4
+MOE_ERR_HIP = 5
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_FLAG_RENORM = 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({detail})")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("F", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(moe_shape)
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_workspace_size": (ctypes.c_int, [_S, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
+    "moe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute": (ctypes.c_int, [_S, _P, _P, _P, _P]),
+    "moe_grouped_gemm_fwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_unpermute_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
+    "moe_unpermute_combine_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_profiler_enable": (ctypes.c_int, [ctypes.c_int]),
+    "moe_profiler_reset": (ctypes.c_int, []),
+    "moe_profiler_count": (ctypes.c_int, []),
+    "moe_profiler_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
+    "moe_version": (ctypes.c_char_p, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build the HIP library first "
+                           "(python -m token_dispatch_grouped_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_names():
+    return list(_SIGNATURES)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def current_stream() -> Optional[int]:
+    import torch
+    if not torch.cuda.is_available():
+        return None
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_shape(T: int, d: int, E: int, k: int, F: int, dtype: int, flags: int = 0) -> moe_shape:
+    return moe_shape(int(T), int(d), int(E), int(k), int(F), int(dtype), int(flags))
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        lib = load()
+        raise MoeError(status, where, lib.moe_last_error().decode() or lib.moe_status_string(status).decode())
+
+
+def _stream(stream):
+    return current_stream() if stream is None else stream
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def moe_workspace_size(shape: moe_shape):
+    lib = load()
+    a, b, c = _SZ(), _SZ(), _SZ()
+    _check(lib.moe_workspace_size(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "moe_workspace_size")
+    return a.value, b.value, c.value
+
+
+def moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, counts, offsets, row_of_slot, src_of_row,
+              ws, ws_bytes, stream=None):
+    lib = load()
+    _check(lib.moe_route(ctypes.byref(shape), ptr(x), ptr(w_router), ptr(bias), ptr(logits), ptr(topk_idx),
+                         ptr(topk_w), ptr(counts), ptr(offsets), ptr(row_of_slot), ptr(src_of_row), ptr(ws),
+                         int(ws_bytes), _stream(stream)), "moe_route")
+
+
+def moe_permute(shape, x, row_of_slot, x_perm, stream=None):
+    lib = load()
+    _check(lib.moe_permute(ctypes.byref(shape), ptr(x), ptr(row_of_slot), ptr(x_perm), _stream(stream)),
+           "moe_permute")
+
+
+def moe_grouped_gemm_fwd(shape, x_perm, w_gu, w_down, offsets, h, a, y, ws, ws_bytes, stream=None):
+    lib = load()
+    _check(lib.moe_grouped_gemm_fwd(ctypes.byref(shape), ptr(x_perm), ptr(w_gu), ptr(w_down), ptr(offsets), ptr(h),
+                                    ptr(a), ptr(y), ptr(ws), int(ws_bytes), _stream(stream)), "moe_grouped_gemm_fwd")
+
+
+def moe_unpermute_combine(shape, y, topk_w, row_of_slot, out, stream=None):
+    lib = load()
+    _check(lib.moe_unpermute_combine(ctypes.byref(shape), ptr(y), ptr(topk_w), ptr(row_of_slot), ptr(out),
+                                     _stream(stream)), "moe_unpermute_combine")
+
+
+def moe_unpermute_combine_bwd(shape, dout, y, topk_w, row_of_slot, dy, dtopk_w, stream=None):
+    lib = load()
+    _check(lib.moe_unpermute_combine_bwd(ctypes.byref(shape), ptr(dout), ptr(y), ptr(topk_w), ptr(row_of_slot),
+                                         ptr(dy), ptr(dtopk_w), _stream(stream)), "moe_unpermute_combine_bwd")
+
+
+def moe_route_bwd(shape, dtopk_w, logits, topk_idx, topk_w, x, w_router, dlogits, dx_router, dw_router, ws,
+                  ws_bytes, stream=None):
+    lib = load()
+    _check(lib.moe_route_bwd(ctypes.byref(shape), ptr(dtopk_w), ptr(logits), ptr(topk_idx), ptr(topk_w), ptr(x),
+                             ptr(w_router), ptr(dlogits), ptr(dx_router), ptr(dw_router), ptr(ws), int(ws_bytes),
+                             _stream(stream)), "moe_route_bwd")
+
+
+def moe_grouped_gemm_bwd(shape, dy, x_perm, h, a, w_gu, w_down, offsets, dx_perm, dw_gu, dw_down, ws, ws_bytes,
+                         stream=None):
+    lib = load()
+    _check(lib.moe_grouped_gemm_bwd(ctypes.byref(shape), ptr(dy), ptr(x_perm), ptr(h), ptr(a), ptr(w_gu),
+                                    ptr(w_down), ptr(offsets), ptr(dx_perm), ptr(dw_gu), ptr(dw_down), ptr(ws),
+                                    int(ws_bytes), _stream(stream)), "moe_grouped_gemm_bwd")
+
+
+def moe_permute_bwd(shape, dx_perm, row_of_slot, dx_extra, dx, stream=None):
+    lib = load()
+    _check(lib.moe_permute_bwd(ctypes.byref(shape), ptr(dx_perm), ptr(row_of_slot), ptr(dx_extra), ptr(dx),
+                               _stream(stream)), "moe_permute_bwd")
+
+
+def moe_status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def moe_last_error() -> str:
+    return load().moe_last_error().decode()
+
+
+def moe_version() -> str:
+    return load().moe_version().decode()
+
+
+def moe_profiler_enable(on: bool):
+    _check(load().moe_profiler_enable(1 if on else 0), "moe_profiler_enable")
+
+
+def moe_profiler_reset():
+    _check(load().moe_profiler_reset(), "moe_profiler_reset")
+
+
+def moe_profiler_read_all():
+    """{kernel name: (launches, total ms)} since the last reset."""
+    lib = load()
+    out = {}
+    for i in range(lib.moe_profiler_count()):
+        name = ctypes.c_char_p()
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib.moe_profiler_read(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)), "moe_profiler_read")
+        out[name.value.decode()] = (n.value, ms.value)
+    return out

@@ -1,0 +1,88 @@
+// Internal launch interface between the C ABI (moe_abi.cpp) and the HIP
+// kernels. Every launcher enqueues on `stream`, makes no launch with an empty
+// grid, and returns the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "validate.h"
+
+namespace moe {
+
+// Geometry of the route pass: tokens per workgroup of the top-k kernel. The
+// per-workgroup expert histograms ([nblk, E] int32) live in the route
+// workspace.
+constexpr int kRouteTokensPerBlock = kRouteTokens;
+// Router weight-gradient partial sums: at most this many token chunks.
+constexpr int kRouterMaxChunks = kRouterChunksMax;
+
+inline int64_t route_blocks(int64_t T) { return (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
+inline int64_t router_chunk_tokens(int64_t T) {
+  int64_t c = (T + kRouterMaxChunks - 1) / kRouterMaxChunks;
+  return c < 256 ? 256 : c;
+}
+inline int64_t router_chunks(int64_t T) {
+  int64_t c = router_chunk_tokens(T);
+  return (T + c - 1) / c;
+}
+
+// Per-kernel timing hook (profiler in moe_abi.cpp). Brackets a launch with
+// events when enabled.
+struct LaunchScope {
+  LaunchScope(const char *name, hipStream_t s);
+  ~LaunchScope();
+  const char *name_;
+  hipStream_t stream_;
+  int slot_;
+};
+
+// ----- routing -----
+hipError_t launch_router_logits(const void *x, const void *w_router, const float *bias, float *logits,
+                                int64_t T, int d, int E, bool bf16, hipStream_t s);
+hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                        int32_t *offsets, int32_t *row_of_slot, int32_t *src_of_row, int32_t *blk_cnt,
+                        int64_t T, int E, int k, bool renorm, hipStream_t s);
+hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
+                            const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
+                            hipStream_t s);
+hipError_t launch_router_bwd(const float *dlogits, const void *x, const void *w_router, float *dx_router,
+                             float *dw_router, float *partial, int64_t T, int d, int E, bool bf16,
+                             hipStream_t s);
+
+// ----- data movement -----
+hipError_t launch_permute(const void *x, const int32_t *row_of_slot, void *x_perm, int64_t T, int d,
+                          int k, bool bf16, hipStream_t s);
+hipError_t launch_combine(const void *y, const float *topk_w, const int32_t *row_of_slot, void *out,
+                          int64_t T, int d, int k, bool bf16, hipStream_t s);
+hipError_t launch_combine_bwd(const void *dout, const void *y, const float *topk_w,
+                              const int32_t *row_of_slot, void *dy, float *dtopk_w, int64_t T, int d,
+                              int k, bool bf16, hipStream_t s);
+hipError_t launch_permute_bwd(const void *dx_perm, const int32_t *row_of_slot, const float *dx_extra,
+                              void *dx, int64_t T, int d, int k, bool bf16, hipStream_t s);
+
+// ----- grouped GEMMs -----
+struct GroupedFfnArgs {
+  const void *x_perm;   // [R, d]
+  const void *w_gu;     // [E, 2F, d]
+  const void *w_down;   // [E, d, F]
+  const int32_t *offsets;  // [E+1]
+  void *h;              // [R, 2F]
+  void *a;              // [R, F]
+  void *y;              // [R, d]
+  // backward
+  const void *dy;       // [R, d]
+  void *dh;             // [R, 2F] (workspace)
+  void *dx_perm;        // [R, d]
+  float *dw_gu;         // [E, 2F, d]
+  float *dw_down;       // [E, d, F]
+  int64_t R;
+  int d, E, F;
+};
+hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s);
+hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s);
+hipError_t launch_ffn_fwd_f32(const GroupedFfnArgs &a, hipStream_t s);
+hipError_t launch_ffn_bwd_f32(const GroupedFfnArgs &a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,369 @@
+// The C ABI of the MoE library: argument validation, workspace carving,
+// kernel launches on the caller's stream, status codes, and the optional
+// per-kernel event timer.
+//
+// Every entry point validates all of its arguments on the host before it
+// launches anything (explicit errors for unsupported configurations: Support
+// combined expert and data parallelism in TrainerRank, Current behavior and
+// Desired behavior). An empty microbatch (T = 0) is a successful no-op, so
+// uneven or empty work never needs special handling by the caller (same page,
+// Desired behavior and Acceptance).
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+#include "validate.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+static moe_status report(moe_status st, const std::string &why) {
+  g_last_error = why;
+  return st;
+}
+
+static moe_status hip_status(hipError_t err, const char *where) {
+  if (err == hipSuccess) return MOE_OK;
+  std::string why = std::string(where) + ": " + hipGetErrorString(err);
+  return report(MOE_ERR_HIP, why);
+}
+
+// ---------------------------------------------------------------------------
+// event timer
+// ---------------------------------------------------------------------------
+struct ProfEntry {
+  const char *name;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> live;  // recorded, not yet read
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+
+struct Profiler {
+  bool on = false;
+  std::vector<ProfEntry> entries;
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  int slot(const char *name) {
+    for (size_t i = 0; i < entries.size(); ++i)
+      if (strcmp(entries[i].name, name) == 0) return (int)i;
+    entries.push_back(ProfEntry{name, {}, 0, 0.0});
+    return (int)entries.size() - 1;
+  }
+  // fold completed event pairs of entry i into its totals
+  void drain(int i) {
+    ProfEntry &en = entries[i];
+    for (auto &pr : en.live) {
+      float ms = 0.f;
+      (void)hipEventSynchronize(pr.second);
+      if (hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess) en.ms += ms;
+      en.launches += 1;
+      pool.push_back(pr.first);
+      pool.push_back(pr.second);
+    }
+    en.live.clear();
+  }
+};
+
+static Profiler g_prof;
+
+LaunchScope::LaunchScope(const char *name, hipStream_t s) : name_(name), stream_(s), slot_(-1) {
+  if (!g_prof.on) return;
+  hipEvent_t a = g_prof.take(), b = g_prof.take();
+  if (!a || !b) return;
+  slot_ = g_prof.slot(name);
+  g_prof.entries[slot_].live.push_back({a, b});
+  (void)hipEventRecord(a, s);
+}
+
+LaunchScope::~LaunchScope() {
+  if (slot_ < 0) return;
+  (void)hipEventRecord(g_prof.entries[slot_].live.back().second, stream_);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+static inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+extern "C" {
+
+const char *moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+const char *moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_workspace_size(const moe_shape *shape, size_t *route_ws, size_t *gemm_fwd_ws,
+                              size_t *gemm_bwd_ws) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(*shape);
+  if (route_ws) *route_ws = w.route_total;
+  if (gemm_fwd_ws) *gemm_fwd_ws = w.gemm_fwd_total;
+  if (gemm_bwd_ws) *gemm_bwd_ws = w.gemm_bwd_total;
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router, const float *bias, float *logits,
+                     int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *row_of_slot,
+                     int32_t *src_of_row, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const bool router = w_router != nullptr;
+  const PtrArg args[] = {
+      {"x", x, router, !router},
+      {"w_router", w_router, false, false},
+      {"bias", bias, false, !router},
+      {"logits", logits, true, false},
+      {"topk_idx", topk_idx, true, false},
+      {"topk_w", topk_w, true, false},
+      {"counts", counts, true, false},
+      {"offsets", offsets, true, false},
+      {"row_of_slot", row_of_slot, true, false},
+      {"src_of_row", src_of_row, true, false},
+  };
+  st = validate_ptrs(args, sizeof(args) / sizeof(args[0]), &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(s);
+  st = validate_workspace(ws, ws_bytes, w.route_total, &why);
+  if (st != MOE_OK) return report(st, why);
+
+  hipStream_t hs = as_stream(stream);
+  const bool bf16 = s.dtype == MOE_DTYPE_BF16;
+  if (router) {
+    st = hip_status(launch_router_logits(x, w_router, bias, logits, s.T, s.d, s.E, bf16, hs), "router_logits");
+    if (st != MOE_OK) return st;
+  }
+  int32_t *blk_cnt = reinterpret_cast<int32_t *>(ws);
+  return hip_status(launch_route(logits, topk_idx, topk_w, counts, offsets, row_of_slot, src_of_row, blk_cnt, s.T,
+                                 s.E, s.k, (s.flags & MOE_FLAG_RENORM) != 0, hs),
+                    "route");
+}
+
+moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *row_of_slot, void *x_perm,
+                       moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const PtrArg args[] = {{"x", x, true, false}, {"row_of_slot", row_of_slot, true, false}, {"x_perm", x_perm, true, false}};
+  st = validate_ptrs(args, 3, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(launch_permute(x, row_of_slot, x_perm, s.T, s.d, s.k, s.dtype == MOE_DTYPE_BF16, as_stream(stream)),
+                    "permute");
+}
+
+static GroupedFfnArgs ffn_args(const moe_shape &s) {
+  GroupedFfnArgs a{};
+  a.R = s.T * (int64_t)s.k;
+  a.d = s.d;
+  a.E = s.E;
+  a.F = s.F;
+  return a;
+}
+
+moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, const void *w_gu, const void *w_down,
+                                const int32_t *offsets, void *h, void *a, void *y, void *ws, size_t ws_bytes,
+                                moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const PtrArg args[] = {{"x_perm", x_perm, true, false}, {"w_gu", w_gu, true, false},
+                         {"w_down", w_down, true, false}, {"offsets", offsets, true, false},
+                         {"h", h, true, false},           {"a", a, true, false},
+                         {"y", y, true, false}};
+  st = validate_ptrs(args, 7, &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(s);
+  st = validate_workspace(ws, ws_bytes, w.gemm_fwd_total, &why);
+  if (st != MOE_OK) return report(st, why);
+  GroupedFfnArgs fa = ffn_args(s);
+  fa.x_perm = x_perm;
+  fa.w_gu = w_gu;
+  fa.w_down = w_down;
+  fa.offsets = offsets;
+  fa.h = h;
+  fa.a = a;
+  fa.y = y;
+  hipStream_t hs = as_stream(stream);
+  return hip_status(s.dtype == MOE_DTYPE_BF16 ? launch_ffn_fwd_bf16(fa, hs) : launch_ffn_fwd_f32(fa, hs),
+                    "grouped_gemm_fwd");
+}
+
+moe_status moe_unpermute_combine(const moe_shape *shape, const void *y, const float *topk_w,
+                                 const int32_t *row_of_slot, void *out, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const PtrArg args[] = {{"y", y, true, false}, {"topk_w", topk_w, true, false},
+                         {"row_of_slot", row_of_slot, true, false}, {"out", out, true, false}};
+  st = validate_ptrs(args, 4, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(
+      launch_combine(y, topk_w, row_of_slot, out, s.T, s.d, s.k, s.dtype == MOE_DTYPE_BF16, as_stream(stream)),
+      "unpermute_combine");
+}
+
+moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dout, const void *y, const float *topk_w,
+                                     const int32_t *row_of_slot, void *dy, float *dtopk_w, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const PtrArg args[] = {{"dout", dout, true, false},       {"y", y, true, false},
+                         {"topk_w", topk_w, true, false},   {"row_of_slot", row_of_slot, true, false},
+                         {"dy", dy, true, false},           {"dtopk_w", dtopk_w, true, false}};
+  st = validate_ptrs(args, 6, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(launch_combine_bwd(dout, y, topk_w, row_of_slot, dy, dtopk_w, s.T, s.d, s.k,
+                                       s.dtype == MOE_DTYPE_BF16, as_stream(stream)),
+                    "unpermute_combine_bwd");
+}
+
+moe_status moe_route_bwd(const moe_shape *shape, const float *dtopk_w, const float *logits, const int32_t *topk_idx,
+                         const float *topk_w, const void *x, const void *w_router, float *dlogits, float *dx_router,
+                         float *dw_router, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const bool router = w_router != nullptr;
+  const PtrArg args[] = {
+      {"dtopk_w", dtopk_w, true, false},  {"logits", logits, true, false},
+      {"topk_idx", topk_idx, true, false}, {"topk_w", topk_w, true, false},
+      {"x", x, router, !router},           {"w_router", w_router, false, false},
+      {"dlogits", dlogits, true, false},   {"dx_router", dx_router, router, !router},
+      {"dw_router", dw_router, router, !router},
+  };
+  st = validate_ptrs(args, sizeof(args) / sizeof(args[0]), &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(s);
+  if (router) {
+    st = validate_workspace(ws, ws_bytes, w.route_total, &why);
+    if (st != MOE_OK) return report(st, why);
+  }
+  hipStream_t hs = as_stream(stream);
+  st = hip_status(launch_route_bwd(dtopk_w, logits, topk_idx, topk_w, dlogits, s.T, s.E, s.k,
+                                   (s.flags & MOE_FLAG_RENORM) != 0, hs),
+                  "route_bwd");
+  if (st != MOE_OK || !router) return st;
+  float *partial = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + w.route_blk_cnt);
+  return hip_status(launch_router_bwd(dlogits, x, w_router, dx_router, dw_router, partial, s.T, s.d, s.E,
+                                      s.dtype == MOE_DTYPE_BF16, hs),
+                    "router_bwd");
+}
+
+moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const void *x_perm, const void *h,
+                                const void *a, const void *w_gu, const void *w_down, const int32_t *offsets,
+                                void *dx_perm, float *dw_gu, float *dw_down, void *ws, size_t ws_bytes,
+                                moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const PtrArg args[] = {{"dy", dy, true, false},         {"x_perm", x_perm, true, false},
+                         {"h", h, true, false},           {"a", a, true, false},
+                         {"w_gu", w_gu, true, false},     {"w_down", w_down, true, false},
+                         {"offsets", offsets, true, false}, {"dx_perm", dx_perm, true, false},
+                         {"dw_gu", dw_gu, true, false},   {"dw_down", dw_down, true, false}};
+  st = validate_ptrs(args, 10, &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(s);
+  st = validate_workspace(ws, ws_bytes, w.gemm_bwd_total, &why);
+  if (st != MOE_OK) return report(st, why);
+  GroupedFfnArgs fa = ffn_args(s);
+  fa.dy = dy;
+  fa.x_perm = x_perm;
+  fa.h = const_cast<void *>(h);
+  fa.a = const_cast<void *>(a);
+  fa.w_gu = w_gu;
+  fa.w_down = w_down;
+  fa.offsets = offsets;
+  fa.dx_perm = dx_perm;
+  fa.dw_gu = dw_gu;
+  fa.dw_down = dw_down;
+  fa.dh = ws;
+  hipStream_t hs = as_stream(stream);
+  return hip_status(s.dtype == MOE_DTYPE_BF16 ? launch_ffn_bwd_bf16(fa, hs) : launch_ffn_bwd_f32(fa, hs),
+                    "grouped_gemm_bwd");
+}
+
+moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const int32_t *row_of_slot,
+                           const float *dx_extra, void *dx, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const PtrArg args[] = {{"dx_perm", dx_perm, true, false}, {"row_of_slot", row_of_slot, true, false},
+                         {"dx_extra", dx_extra, false, false}, {"dx", dx, true, false}};
+  st = validate_ptrs(args, 4, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(launch_permute_bwd(dx_perm, row_of_slot, dx_extra, dx, s.T, s.d, s.k, s.dtype == MOE_DTYPE_BF16,
+                                       as_stream(stream)),
+                    "permute_bwd");
+}
+
+moe_status moe_profiler_enable(int on) {
+  g_prof.on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profiler_reset(void) {
+  for (size_t i = 0; i < g_prof.entries.size(); ++i) g_prof.drain((int)i);
+  g_prof.entries.clear();
+  return MOE_OK;
+}
+
+int moe_profiler_count(void) { return (int)g_prof.entries.size(); }
+
+moe_status moe_profiler_read(int i, const char **name, int64_t *launches, double *total_ms) {
+  if (i < 0 || i >= (int)g_prof.entries.size()) return report(MOE_ERR_INVALID_ARGUMENT, "profiler index out of range");
+  g_prof.drain(i);
+  const ProfEntry &en = g_prof.entries[i];
+  if (name) *name = en.name;
+  if (launches) *launches = en.launches;
+  if (total_ms) *total_ms = en.ms;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,487 @@
+// Routing kernels: router logits, top-k softmax selection with a
+// deterministic stable counting sort into expert-contiguous rows, and the
+// routing backward.
+//
+// The pages name the step ("EP token dispatch", Add MoE expert parallel
+// training runtime, Major changes) and require that any per-expert row count,
+// zero included, works without padding and that outputs return in full
+// source order (Support combined expert and data parallelism in TrainerRank,
+// Desired behavior). The rule implemented: the k largest logits of a token,
+// descending, equal logits to the lower expert id; weights are the softmax
+// probabilities of the selected experts (optionally renormalised); rows of
+// one expert follow ascending source token.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// A1: logits = x w_router^T + bias. One wavefront per token; lanes split the
+// hidden dimension in 16-byte chunks, experts are taken 16 at a time and each
+// partial dot product is reduced across the wavefront.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void router_logits_kernel(const T *__restrict__ x, const T *__restrict__ wr,
+                                                            const float *__restrict__ bias,
+                                                            float *__restrict__ logits, int64_t ntok, int d,
+                                                            int E) {
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const T *xr = x + t * d;
+  const int nchunk = d / V;
+  for (int e0 = 0; e0 < E; e0 += 16) {
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int c = lane; c < nchunk; c += 64) {
+      float xv[V];
+      Elem<T>::unpack(ld16(xr + (size_t)c * V), xv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (e0 + i < E) {
+          float wv[V];
+          Elem<T>::unpack(ld16(wr + (size_t)(e0 + i) * d + (size_t)c * V), wv);
+#pragma unroll
+          for (int q = 0; q < V; ++q) acc[i] = fmaf(xv[q], wv[q], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (e0 + i < E) {
+        float s = wave_sum(acc[i]);
+        if (lane == 0) logits[t * E + e0 + i] = s + (bias ? bias[e0 + i] : 0.f);
+      }
+    }
+  }
+}
+
+// Order-preserving map of fp32 onto uint32: larger value -> larger key, NaN
+// below everything (key 0), -0.0 equal to +0.0.
+MOE_DEVICE uint32_t order_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// A2 + first half of A3: per token top-k and weights; per workgroup the
+// stable rank of each (token, slot) among the workgroup's slots of the same
+// expert, and the workgroup's expert histogram.
+//
+// One thread per token, 256 tokens per workgroup (4 wavefronts). Top-k keeps
+// a descending list of 64-bit composite keys (logit key, then inverted id so
+// that the lower id wins a tie). Ranks within a wavefront come from ballots
+// over the bits of the expert id (every lane learns, for its own expert,
+// which lanes hold the same expert in each slot column); ranks across
+// wavefronts from per-wavefront counts in LDS. No atomics decide any order.
+// ---------------------------------------------------------------------------
+template <int KMAX>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
+                                                         int32_t *__restrict__ topk_idx,
+                                                         float *__restrict__ topk_w,
+                                                         int32_t *__restrict__ local_rank,
+                                                         int32_t *__restrict__ blk_cnt, int64_t ntok, int E,
+                                                         int k, int id_bits, int renorm) {
+  __shared__ int32_t s_wcnt[4][256];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  const bool valid = t < ntok;
+
+  for (int i = tid; i < 4 * 256; i += 256) (&s_wcnt[0][0])[i] = 0;
+
+  uint64_t list[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) list[i] = 0ull;
+  int ids[KMAX];
+  float w[KMAX];
+  if (valid) {
+    const float *row = logits + t * E;
+    for (int e = 0; e < E; ++e) {
+      uint64_t c = ((uint64_t)order_key(row[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+      if (c > list[KMAX - 1]) {
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+          uint64_t hi = c > list[i] ? c : list[i];
+          uint64_t lo = c > list[i] ? list[i] : c;
+          list[i] = hi;
+          c = lo;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) ids[i] = (int)(0xffffffffu - (uint32_t)(list[i] & 0xffffffffu));
+    // softmax over the whole row; the first selected logit is the maximum
+    const float m = row[ids[0]];
+    float sum = 0.f;
+    for (int e = 0; e < E; ++e) {
+      float l = row[e];
+      sum += (l == l) ? expf(l - m) : 0.f;
+    }
+    float wsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      float l = row[(unsigned)ids[i] < (unsigned)E ? ids[i] : 0];
+      w[i] = (i < k && l == l) ? expf(l - m) / sum : 0.f;
+      if (i < k) wsum += w[i];
+    }
+    if (renorm) {
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) w[i] = w[i] / wsum;
+    }
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i < k) {
+        topk_idx[t * k + i] = ids[i];
+        topk_w[t * k + i] = w[i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) ids[i] = 0;
+  }
+  __syncthreads();  // s_wcnt cleared
+
+  // ranks within the wavefront
+  const uint64_t vmask = __ballot(valid);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int below[KMAX], total[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) below[j] = total[j] = 0;
+#pragma unroll
+  for (int jc = 0; jc < KMAX; ++jc) {
+    if (jc >= k) break;
+    uint64_t bal[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) bal[b] = (b < id_bits) ? __ballot((ids[jc] >> b) & 1) : 0ull;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        uint64_t mm = vmask;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          if (b < id_bits) mm &= ((ids[j] >> b) & 1) ? bal[b] : ~bal[b];
+        below[j] += __popcll(mm & lt);
+        total[j] += __popcll(mm);
+      }
+    }
+  }
+  // the first lane of the wavefront holding expert e publishes the count
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k && below[j] == 0) s_wcnt[wave][ids[j]] = total[j];
+  }
+  __syncthreads();
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        int pre = 0;
+        for (int w2 = 0; w2 < wave; ++w2) pre += s_wcnt[w2][ids[j]];
+        local_rank[t * k + j] = pre + below[j];
+      }
+    }
+  }
+  for (int e = tid; e < E; e += 256)
+    blk_cnt[(int64_t)blockIdx.x * E + e] = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads); returns the
+// exclusive prefix and writes the block total to *total.
+MOE_DEVICE int block_exclusive_scan_256(int v, int *s_tmp, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = wave_inclusive_scan(v);
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int wpre = 0, all = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    int tv = s_tmp[w2];
+    if (w2 < wave) wpre += tv;
+    all += tv;
+  }
+  __syncthreads();
+  *total = all;
+  return wpre + inc - v;
+}
+
+// Second half of A3, step 1: per expert, exclusive scan of the workgroup
+// histograms over workgroups (in place), and the expert's total row count.
+__global__ __launch_bounds__(256) void route_scan_kernel(int32_t *__restrict__ blk_cnt,
+                                                         int32_t *__restrict__ counts, int64_t nblk, int E) {
+  __shared__ int s_tmp[4];
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int64_t b0 = 0; b0 < nblk; b0 += 256) {
+    const int64_t b = b0 + threadIdx.x;
+    int v = b < nblk ? blk_cnt[b * E + e] : 0;
+    int tot;
+    int ex = block_exclusive_scan_256(v, s_tmp, &tot);
+    if (b < nblk) blk_cnt[b * E + e] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// Second half of A3, step 2: offsets, final rows and the inverse map.
+// row = offsets[e] + (rows of e in earlier workgroups) + (rank in workgroup).
+__global__ __launch_bounds__(256) void route_rows_kernel(const int32_t *__restrict__ topk_idx,
+                                                         const int32_t *__restrict__ counts,
+                                                         const int32_t *__restrict__ blk_cnt,
+                                                         int32_t *__restrict__ row_of_slot,
+                                                         int32_t *__restrict__ src_of_row,
+                                                         int32_t *__restrict__ offsets, int64_t nslot, int E,
+                                                         int k) {
+  __shared__ int s_off[257];
+  __shared__ int s_tmp[4];
+  const int tid = threadIdx.x;
+  int v = tid < E ? counts[tid] : 0;
+  int tot;
+  int ex = block_exclusive_scan_256(v, s_tmp, &tot);
+  s_off[tid] = ex;
+  if (tid == 0) s_off[256] = tot;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) offsets[tid] = ex;
+    if (tid == 0) offsets[E] = tot;
+  }
+  const int64_t s = (int64_t)blockIdx.x * 256 + tid;
+  if (s >= nslot) return;
+  const int e = topk_idx[s];
+  const int64_t t = s / k;
+  const int64_t b = t / kRouteTokensPerBlock;
+  const int row = s_off[e] + blk_cnt[b * E + e] + row_of_slot[s];
+  row_of_slot[s] = row;
+  if ((uint64_t)row < (uint64_t)nslot) src_of_row[row] = (int32_t)s;
+}
+
+// ---------------------------------------------------------------------------
+// B2: dlogits from dtopk_w. One thread per token.
+// ---------------------------------------------------------------------------
+template <int KMAX>
+__global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict__ dtopk_w,
+                                                        const float *__restrict__ logits,
+                                                        const int32_t *__restrict__ topk_idx,
+                                                        const float *__restrict__ topk_w,
+                                                        float *__restrict__ dlogits, int64_t ntok, int E, int k,
+                                                        int renorm) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= ntok) return;
+  const float *row = logits + t * E;
+  float *drow = dlogits + t * E;
+  int ids[KMAX];
+  float g[KMAX], w[KMAX];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      ids[j] = topk_idx[t * k + j];
+      g[j] = dtopk_w[t * k + j];
+      w[j] = topk_w[t * k + j];
+      s = fmaf(w[j], g[j], s);
+    }
+  }
+  if (renorm) {
+    for (int e = 0; e < E; ++e) drow[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) drow[ids[j]] = w[j] * (g[j] - s);
+    return;
+  }
+  float m = -INFINITY;
+  for (int e = 0; e < E; ++e) {
+    float l = row[e];
+    if (l == l) m = fmaxf(m, l);
+  }
+  float sum = 0.f;
+  for (int e = 0; e < E; ++e) {
+    float l = row[e];
+    sum += (l == l) ? expf(l - m) : 0.f;
+  }
+  const float inv = 1.f / sum;
+  for (int e = 0; e < E; ++e) {
+    float l = row[e];
+    float p = (l == l) ? expf(l - m) * inv : 0.f;
+    drow[e] = -p * s;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      float l = row[ids[j]];
+      float p = (l == l) ? expf(l - m) * inv : 0.f;
+      drow[ids[j]] = p * (g[j] - s);
+    }
+  }
+}
+
+// Router backward: dx_router[t,c] = sum_e dlogits[t,e] w_router[e,c].
+template <typename T>
+__global__ __launch_bounds__(256) void router_dx_kernel(const float *__restrict__ dlogits,
+                                                        const T *__restrict__ wr, float *__restrict__ dx,
+                                                        int64_t ntok, int d, int E) {
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int64_t t = blockIdx.x;
+  if (c >= d || t >= ntok) return;
+  float acc = 0.f;
+  for (int e = 0; e < E; ++e) acc = fmaf(dlogits[t * E + e], Elem<T>::load(wr + (size_t)e * d + c), acc);
+  dx[t * d + c] = acc;
+}
+
+// Router weight gradient, pass 1: partial[chunk, e, c] = sum over the
+// chunk's tokens of dlogits[t,e] x[t,c]; 8 experts per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void router_dw_partial_kernel(const float *__restrict__ dlogits,
+                                                                const T *__restrict__ x,
+                                                                float *__restrict__ partial, int64_t ntok,
+                                                                int d, int E, int64_t chunk_tokens) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int64_t chunk = blockIdx.y;
+  const int e0 = blockIdx.z * 8;
+  if (c >= d) return;
+  const int64_t t0 = chunk * chunk_tokens;
+  const int64_t t1 = t0 + chunk_tokens < ntok ? t0 + chunk_tokens : ntok;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int64_t t = t0; t < t1; ++t) {
+    const float xv = Elem<T>::load(x + t * d + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (e0 + i < E) acc[i] = fmaf(dlogits[t * E + e0 + i], xv, acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (e0 + i < E) partial[(chunk * E + e0 + i) * (int64_t)d + c] = acc[i];
+}
+
+// Router weight gradient, pass 2: dw_router[e,c] += sum over chunks, in
+// chunk order.
+__global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float *__restrict__ partial,
+                                                               float *__restrict__ dw, int64_t nchunk, int d,
+                                                               int E) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int e = blockIdx.y;
+  if (c >= d) return;
+  float acc = 0.f;
+  for (int64_t ch = 0; ch < nchunk; ++ch) acc += partial[(ch * E + e) * (int64_t)d + c];
+  dw[(int64_t)e * d + c] += acc;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const void *x, const void *w_router, const float *bias, float *logits,
+                                int64_t T, int d, int E, bool bf16, hipStream_t s) {
+  LaunchScope scope("router_logits", s);
+  dim3 grid((unsigned)((T + 3) / 4));
+  if (bf16)
+    router_logits_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t *)x, (const bf16_t *)w_router, bias, logits,
+                                                      T, d, E);
+  else
+    router_logits_kernel<float><<<grid, 256, 0, s>>>((const float *)x, (const float *)w_router, bias, logits, T,
+                                                     d, E);
+  return hipGetLastError();
+}
+
+template <int KMAX>
+static void launch_topk_k(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *rank, int32_t *blk_cnt,
+                          int64_t T, int E, int k, int bits, bool renorm, hipStream_t s) {
+  dim3 grid((unsigned)route_blocks(T));
+  route_topk_kernel<KMAX><<<grid, 256, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, bits,
+                                               renorm ? 1 : 0);
+}
+
+hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                        int32_t *offsets, int32_t *row_of_slot, int32_t *src_of_row, int32_t *blk_cnt,
+                        int64_t T, int E, int k, bool renorm, hipStream_t s) {
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const int64_t nblk = route_blocks(T);
+  {
+    LaunchScope scope("route_topk", s);
+    if (k <= 1)
+      launch_topk_k<1>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+    else if (k <= 2)
+      launch_topk_k<2>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+    else if (k <= 4)
+      launch_topk_k<4>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+    else if (k <= 8)
+      launch_topk_k<8>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+    else
+      launch_topk_k<16>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    LaunchScope scope("route_scan", s);
+    route_scan_kernel<<<dim3((unsigned)E), 256, 0, s>>>(blk_cnt, counts, nblk, E);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t nslot = T * k;
+  {
+    LaunchScope scope("route_rows", s);
+    route_rows_kernel<<<dim3((unsigned)((nslot + 255) / 256)), 256, 0, s>>>(topk_idx, counts, blk_cnt, row_of_slot,
+                                                                          src_of_row, offsets, nslot, E, k);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
+                            const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
+                            hipStream_t s) {
+  LaunchScope scope("route_bwd", s);
+  dim3 grid((unsigned)((T + 255) / 256));
+  const int r = renorm ? 1 : 0;
+  if (k <= 2)
+    route_bwd_kernel<2><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+  else if (k <= 4)
+    route_bwd_kernel<4><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+  else if (k <= 8)
+    route_bwd_kernel<8><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+  else
+    route_bwd_kernel<16><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float *dlogits, const void *x, const void *w_router, float *dx_router,
+                             float *dw_router, float *partial, int64_t T, int d, int E, bool bf16,
+                             hipStream_t s) {
+  const int64_t chunk = router_chunk_tokens(T);
+  const int64_t nchunk = router_chunks(T);
+  const unsigned cblocks = (unsigned)((d + 255) / 256);
+  {
+    LaunchScope scope("router_dx", s);
+    if (bf16)
+      router_dx_kernel<bf16_t><<<dim3((unsigned)T, cblocks), 256, 0, s>>>(dlogits, (const bf16_t *)w_router,
+                                                                         dx_router, T, d, E);
+    else
+      router_dx_kernel<float><<<dim3((unsigned)T, cblocks), 256, 0, s>>>(dlogits, (const float *)w_router,
+                                                                        dx_router, T, d, E);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    LaunchScope scope("router_dw_partial", s);
+    dim3 grid(cblocks, (unsigned)nchunk, (unsigned)((E + 7) / 8));
+    if (bf16)
+      router_dw_partial_kernel<bf16_t><<<grid, 256, 0, s>>>(dlogits, (const bf16_t *)x, partial, T, d, E, chunk);
+    else
+      router_dw_partial_kernel<float><<<grid, 256, 0, s>>>(dlogits, (const float *)x, partial, T, d, E, chunk);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    LaunchScope scope("router_dw_reduce", s);
+    router_dw_reduce_kernel<<<dim3(cblocks, (unsigned)E), 256, 0, s>>>(partial, dw_router, nchunk, d, E);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,103 @@
+// Host-side validation of every C-ABI argument, done before anything is
+// launched. Unsupported configurations are rejected explicitly and up front
+// (Support combined expert and data parallelism in TrainerRank, Current
+// behavior and Desired behavior), and every argument is checked before any
+// is consumed (review note on Add MoE expert parallel training runtime).
+#include "validate.h"
+
+#include <stdio.h>
+
+namespace moe {
+
+static moe_status fail(std::string *why, moe_status st, const char *msg) {
+  if (why) *why = msg;
+  return st;
+}
+
+moe_status validate_shape(const moe_shape *s, std::string *why) {
+  if (!s) return fail(why, MOE_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->T < 0) return fail(why, MOE_ERR_INVALID_ARGUMENT, "T < 0");
+  if (s->d <= 0 || s->E <= 0 || s->k <= 0 || s->F <= 0)
+    return fail(why, MOE_ERR_INVALID_ARGUMENT, "d, E, k and F must be positive");
+  if (s->k > s->E) return fail(why, MOE_ERR_INVALID_ARGUMENT, "k > E");
+  if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16)
+    return fail(why, MOE_ERR_UNSUPPORTED, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (s->flags & ~(uint32_t)MOE_FLAG_RENORM) return fail(why, MOE_ERR_UNSUPPORTED, "unknown flag bits");
+  if (s->E > 256) return fail(why, MOE_ERR_UNSUPPORTED, "E > 256");
+  if (s->k > 16) return fail(why, MOE_ERR_UNSUPPORTED, "k > 16");
+  if (s->d % 64 != 0 || s->F % 64 != 0) return fail(why, MOE_ERR_UNSUPPORTED, "d and F must be multiples of 64");
+  if (s->d > 65536 || s->F > 65536) return fail(why, MOE_ERR_UNSUPPORTED, "d or F > 65536");
+  const int64_t R = s->T * (int64_t)s->k;
+  if (s->T > ((int64_t)1 << 31) || R >= ((int64_t)1 << 31)) return fail(why, MOE_ERR_UNSUPPORTED, "T*k >= 2^31");
+  // every grid must fit in 2^31 - 8 workgroups
+  const int64_t lim = ((int64_t)1 << 31) - 8;
+  const int64_t wide = s->d > 2 * (int64_t)s->F ? s->d : 2 * (int64_t)s->F;
+  int64_t gemm_blocks;
+  if (s->dtype == MOE_DTYPE_BF16) {
+    gemm_blocks = (R / kGemmBM + s->E) * ceil_div(wide, kGemmBN / 2);
+    const int64_t wg = (int64_t)s->E * ceil_div(wide, kGemmBM) * ceil_div(wide, kGemmBN);
+    if (wg > gemm_blocks) gemm_blocks = wg;
+  } else {
+    gemm_blocks = (R / kGemmF32Tile + s->E) * ceil_div(wide, kGemmF32Tile);
+    const int64_t wg = (int64_t)s->E * ceil_div(wide, kGemmF32Tile) * ceil_div(wide, kGemmF32Tile);
+    if (wg > gemm_blocks) gemm_blocks = wg;
+  }
+  const int64_t vec = s->dtype == MOE_DTYPE_BF16 ? 8 : 4;
+  const int64_t mem_blocks = ceil_div(s->T * (s->d / vec), 256);
+  if (gemm_blocks > lim || mem_blocks > lim) return fail(why, MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MOE_OK;
+}
+
+WorkspaceLayout workspace_layout(const moe_shape &s) {
+  WorkspaceLayout w{};
+  const int64_t nblk = ceil_div(s.T, kRouteTokens);
+  w.route_blk_cnt = align256((size_t)nblk * (size_t)s.E * 4);
+  int64_t chunk_tokens = ceil_div(s.T, kRouterChunksMax);
+  if (chunk_tokens < 256) chunk_tokens = 256;
+  const int64_t nchunk = ceil_div(s.T, chunk_tokens);
+  w.route_partial = align256((size_t)nchunk * (size_t)s.E * (size_t)s.d * 4);
+  w.route_total = w.route_blk_cnt + w.route_partial;
+  w.gemm_fwd_total = 0;
+  const size_t es = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  w.gemm_bwd_dh = align256((size_t)s.T * (size_t)s.k * 2 * (size_t)s.F * es);
+  w.gemm_bwd_total = w.gemm_bwd_dh;
+  return w;
+}
+
+moe_status validate_ptrs(const PtrArg *args, int n, std::string *why) {
+  for (int i = 0; i < n; ++i) {
+    const PtrArg &a = args[i];
+    char buf[160];
+    if (a.needed && !a.ptr) {
+      snprintf(buf, sizeof buf, "%s is NULL", a.name);
+      return fail(why, MOE_ERR_INVALID_ARGUMENT, buf);
+    }
+    if (a.must_be_null && a.ptr) {
+      snprintf(buf, sizeof buf, "%s must be NULL in this mode", a.name);
+      return fail(why, MOE_ERR_INVALID_ARGUMENT, buf);
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    const PtrArg &a = args[i];
+    if (a.ptr && ((uintptr_t)a.ptr & 15u) != 0) {
+      char buf[160];
+      snprintf(buf, sizeof buf, "%s is not 16-byte aligned", a.name);
+      return fail(why, MOE_ERR_MISALIGNED, buf);
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status validate_workspace(const void *ws, size_t have, size_t need, std::string *why) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(why, MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws & 15u) != 0) return fail(why, MOE_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  if (have < need) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "workspace too small: %zu bytes given, %zu needed", have, need);
+    return fail(why, MOE_ERR_WORKSPACE, buf);
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,55 @@
+// Host-side argument validation and workspace sizing for the C ABI. Pure
+// C++ (no HIP), so it can be built and unit-tested without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Tile sizes the launchers use; validation checks that grids fit.
+constexpr int kRouteTokens = 256;       // tokens per top-k workgroup
+constexpr int kRouterChunksMax = 32;    // router weight-gradient partial sums
+constexpr int kGemmBM = 128;            // bf16 grouped GEMM rows per tile
+constexpr int kGemmBN = 128;            // bf16 grouped GEMM columns per tile
+constexpr int kGemmF32Tile = 16;        // fp32 grouped GEMM tile edge
+
+struct WorkspaceLayout {
+  size_t route_blk_cnt;   // bytes of the per-workgroup expert histograms
+  size_t route_partial;   // bytes of router weight-gradient partial sums
+  size_t route_total;
+  size_t gemm_fwd_total;
+  size_t gemm_bwd_dh;     // bytes of dH
+  size_t gemm_bwd_total;
+};
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validates the shape alone. On failure writes a message to *why.
+moe_status validate_shape(const moe_shape *s, std::string *why);
+
+// Workspace layout of a (validated) shape.
+WorkspaceLayout workspace_layout(const moe_shape &s);
+
+// One pointer argument: `needed` tells whether the call reads or writes it.
+// NULL where needed -> MOE_ERR_INVALID_ARGUMENT; non-NULL where it must be
+// NULL (must_be_null) -> MOE_ERR_INVALID_ARGUMENT; not 16-byte aligned ->
+// MOE_ERR_MISALIGNED.
+struct PtrArg {
+  const char *name;
+  const void *ptr;
+  bool needed;
+  bool must_be_null;
+};
+moe_status validate_ptrs(const PtrArg *args, int n, std::string *why);
+
+// Workspace check: NULL or short -> MOE_ERR_WORKSPACE (a zero requirement
+// accepts anything).
+moe_status validate_workspace(const void *ws, size_t have, size_t need, std::string *why);
+
+}  // namespace moe
