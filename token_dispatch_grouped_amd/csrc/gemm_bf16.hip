@@ -4,8 +4,8 @@
 // One kernel template covers the six products of the SwiGLU expert FFN,
 // forward and backward. For expert e it computes
 //     C_e[m, n] = sum_k A_e(m, k) * B_e(n, k)
-// where each operand is read either k-contiguous ("N" layout, row-major
-// [rows, K]) or transposed (row-major [K, rows]):
+// where each operand is read either k-contiguous (row-major [rows, K]) or
+// transposed (row-major [K, rows]):
 //   gate/up fwd   H  = X W_gu^T      A = x_perm [R,d]  B = W_gu[e] [2F,d]   ragged M
 //   down fwd      Y  = A W_down^T    A = a [R,F]       B = W_down[e] [d,F]  ragged M
 //   down dgrad    dA = dY W_down     A = dy [R,d]      B^T = W_down[e]      ragged M
@@ -17,13 +17,23 @@
 // `offsets` on the device, so an expert with no rows gets no tile at all and
 // any M_e (0 included) needs no padding.
 //
-// Tiling: a 256-thread workgroup (4 wavefronts) computes a BM x BN tile with
-// BK = 64 deep k-steps, double-buffered in LDS. Both operands are stored in
-// LDS k-contiguous, in 16-byte chunks with an XOR swizzle so that the
-// fragment reads of v_mfma_f32_32x32x16_bf16 and the tile writes are free of
-// bank conflicts. Transposed operands are turned k-contiguous on the way in:
-// each thread loads an 8(k) x 8 block with eight 16-byte loads and transposes
-// it in registers. Accumulation is fp32; the epilogue rounds once.
+// Tiling: a 256-thread workgroup (4 wavefronts, 2x2) computes a BM x BN
+// tile; each wavefront owns a WM x WN sub-tile of v_mfma_f32_32x32x16_bf16
+// results held in fp32. k advances in steps of 64, double-buffered in LDS:
+// the next step's global loads are issued before the current step's MFMAs.
+// Both operands sit in LDS k-contiguous, in 16-byte chunks with an XOR
+// swizzle that keeps the fragment reads and the tile writes free of bank
+// conflicts. Transposed operands are made k-contiguous on the way in: each
+// thread loads an 8(k) x 8 block with eight 16-byte loads and transposes it
+// in registers.
+//
+// Epilogues: bf16 outputs are staged through LDS and written with 16-byte,
+// fully coalesced stores (the MFMA is issued with its operands swapped so
+// that each lane holds four consecutive output columns). The SwiGLU forward
+// writes h and a = silu(gate) * up from the fp32 accumulators; the SwiGLU
+// backward reads its h tile into LDS with coalesced loads and rewrites it in
+// place as dH. Weight gradients are read-modify-written in fp32, each element
+// by exactly one workgroup (no atomics), heaviest experts first.
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -39,6 +49,7 @@ struct GemmParams {
   bf16_t *C2;             // EPI_SWIGLU_FWD: the activation a
   const bf16_t *H;        // EPI_SWIGLU_BWD: saved h
   const int32_t *offsets;
+  const int32_t *order;   // ragged K: experts by descending row count
   int E;
   int M;                  // ragged K: rows of C
   int N;                  // columns of C (EPI_SWIGLU_FWD: F, the gate half)
@@ -55,36 +66,208 @@ constexpr int kBK = 64;
 
 MOE_DEVICE int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Combine two bf16 lanes: element `j` of dword words a and b.
+// Combine two bf16 lanes: element `odd` of dwords a and b.
 MOE_DEVICE uint32_t pick_pair(uint32_t a, uint32_t b, int odd) {
   return odd ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
 }
 
+// Epilogue shared by the grouped GEMM kernels. With EPI_ACC_F32 the
+// accumulators are in MFMA order (lane = column); otherwise in swapped order
+// (lane = row, four consecutive columns per accumulator group) and `lds`
+// (at least BM*BN*2 bytes, or BM*BN*4 for EPI_SWIGLU_BWD) stages the tile.
+template <int BM, int BN, int WM, int WN, int EPI, int NT = 256>
+MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32], u32x4_t *lds, int e, int m0,
+                         int n_tile, int m_valid, int64_t crow0, int wm, int wn) {
+  constexpr int FM = WM / 32, FN = WN / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  if (EPI == EPI_ACC_F32) {
+    // acc[i][j][v] sits at tile row wm*WM + i*32 + 8*(v/4) + 4*lhi + (v%4),
+    // tile column wn*WN + j*32 + l32.
+    float *C = (float *)p.C + (int64_t)e * p.strideC;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n_tile * BN + wn * WN + j * 32 + l32;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
+          if (r < m_valid) {
+            float *dst = C + (int64_t)(m0 + r) * p.ldc + n;
+            *dst = *dst + acc[i][j][v];
+          }
+        }
+    }
+    return;
+  }
+
+  // Swapped layout: acc[i][j][4g + q] is tile row wm*WM + i*32 + l32 and
+  // tile column wn*WN + j*32 + 8g + 4*lhi + q (q = 0..3 consecutive).
+  // LDS staging: rows of sw bf16 (sw/8 chunks), chunk c of row r stored at
+  // chunk c ^ (r & 15).
+  bf16_t *stg = reinterpret_cast<bf16_t *>(lds);
+  auto stg_off = [](int r, int col, int sw) -> int {  // element offset, col % 4 == 0
+    const int c = col >> 3;
+    return r * sw + ((c ^ (r & 15)) << 3) + (col & 7);
+  };
+  auto stg_put4 = [&](int r, int col, int sw, float x0, float x1, float x2, float x3) {
+    uint2 v;
+    v.x = pack_bf2(x0, x1);
+    v.y = pack_bf2(x2, x3);
+    *reinterpret_cast<uint2 *>(stg + stg_off(r, col, sw)) = v;
+  };
+  // coalesced copy of a staged [BM][sw] tile to global memory; col_map gives
+  // the destination column of staged column c (a multiple of 8), or -1.
+  auto flush = [&](int sw, bf16_t *dst, int64_t ld, auto col_map) {
+    const int cpr = sw / 8;
+    for (int c = tid; c < BM * cpr; c += NT) {
+      const int r = c / cpr, ch = c - r * cpr;
+      if (r >= m_valid) continue;
+      const int gc = col_map(ch * 8);
+      if (gc < 0) continue;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + r * sw + ((ch ^ (r & 15)) << 3));
+      st16(dst + (crow0 + r) * ld + gc, v);
+    }
+  };
+
+  if (EPI == EPI_STORE) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = wm * WM + i * 32 + l32;
+          const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
+          stg_put4(r, col, BN, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+    __syncthreads();
+    const int n0 = n_tile * BN;
+    flush(BN, (bf16_t *)p.C, p.ldc, [&](int c) { return n0 + c < p.N ? n0 + c : -1; });
+  } else if (EPI == EPI_SWIGLU_FWD) {
+    // staged h tile: gate columns [0, BN/2), up columns [BN/2, BN)
+    const int g0 = n_tile * (BN / 2);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = wm * WM + i * 32 + l32;
+          const int col = wn * (WN / 2) + j * 32 + 8 * g + 4 * lhi;
+          const f32x16_t &ga = acc[i][j];
+          const f32x16_t &ua = acc[i][j + FN / 2];
+          stg_put4(r, col, BN, ga[4 * g], ga[4 * g + 1], ga[4 * g + 2], ga[4 * g + 3]);
+          stg_put4(r, BN / 2 + col, BN, ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
+        }
+    __syncthreads();
+    flush(BN, (bf16_t *)p.C, p.ldc, [&](int c) {
+      if (c < BN / 2) return g0 + c < p.N ? g0 + c : -1;
+      const int g = g0 + c - BN / 2;
+      return g < p.N ? p.F + g : -1;
+    });
+    __syncthreads();
+    // staged a = silu(gate) * up tile, BN/2 columns
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = wm * WM + i * 32 + l32;
+          const int col = wn * (WN / 2) + j * 32 + 8 * g + 4 * lhi;
+          const f32x16_t &ga = acc[i][j];
+          const f32x16_t &ua = acc[i][j + FN / 2];
+          stg_put4(r, col, BN / 2, silu_f(ga[4 * g]) * ua[4 * g], silu_f(ga[4 * g + 1]) * ua[4 * g + 1],
+                   silu_f(ga[4 * g + 2]) * ua[4 * g + 2], silu_f(ga[4 * g + 3]) * ua[4 * g + 3]);
+        }
+    __syncthreads();
+    flush(BN / 2, p.C2, p.F, [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
+  } else {  // EPI_SWIGLU_BWD: stage h (gate | up) in LDS, rewrite it as dH
+    constexpr int SW = 2 * BN;
+    const int n0 = n_tile * BN;
+    constexpr int cpr = SW / 8;
+    for (int c = tid; c < BM * cpr; c += NT) {
+      const int r = c / cpr, ch = c - r * cpr;
+      const int col = ch * 8;
+      const int gcol = col < BN ? n0 + col : n0 + col - BN;
+      u32x4_t v = zero4;
+      if (r < m_valid && gcol < p.N) v = ld16(p.H + (crow0 + r) * p.ldc + (col < BN ? gcol : p.F + gcol));
+      *reinterpret_cast<u32x4_t *>(stg + r * SW + ((ch ^ (r & 15)) << 3)) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = wm * WM + i * 32 + l32;
+          const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
+          uint2 *pg = reinterpret_cast<uint2 *>(stg + stg_off(r, col, SW));
+          uint2 *pu = reinterpret_cast<uint2 *>(stg + stg_off(r, BN + col, SW));
+          const uint2 hg2 = *pg, hu2 = *pu;
+          const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
+                               __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
+          const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
+                               __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float da = acc[i][j][4 * g + q];
+            const float sg = sigmoid_f(hg[q]);
+            dg[q] = da * hu[q] * sg * (1.f + hg[q] * (1.f - sg));
+            du[q] = da * hg[q] * sg;
+          }
+          uint2 og, ou;
+          og.x = pack_bf2(dg[0], dg[1]);
+          og.y = pack_bf2(dg[2], dg[3]);
+          ou.x = pack_bf2(du[0], du[1]);
+          ou.y = pack_bf2(du[2], du[3]);
+          *pg = og;
+          *pu = ou;
+        }
+    __syncthreads();
+    flush(SW, (bf16_t *)p.C, p.ldc, [&](int c) {
+      if (c < BN) return n0 + c < p.N ? n0 + c : -1;
+      const int n = n0 + c - BN;
+      return n < p.N ? p.F + n : -1;
+    });
+  }
+}
+
 template <int BM, int BN, int WM, int WN, bool AT, bool BT, int EPI, bool RAGGED_K>
-__global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, 1) void gg_bf16_kernel(GemmParams p) {
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
   static_assert(WAVES_M * WAVES_N == 4, "4 wavefronts per workgroup");
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
-  // 16-byte chunks per operand tile
-  constexpr int A_CHUNKS = BM * kBK / 8;
+  // bf16 epilogues use the swapped MFMA (lane = output row, 4 consecutive
+  // columns per accumulator group); the fp32 accumulate keeps lane = column.
+  constexpr bool SWAP = EPI != EPI_ACC_F32;
+  constexpr int A_CHUNKS = BM * kBK / 8;  // 16-byte chunks per operand tile
   constexpr int B_CHUNKS = BN * kBK / 8;
-  // per-thread staging (N layout: chunks; transposed layout: 8x8 blocks)
   constexpr int A_NL = AT ? 0 : A_CHUNKS / 256;
   constexpr int B_NL = BT ? 0 : B_CHUNKS / 256;
-  constexpr int A_SUB = AT ? BM * kBK / 64 : 0;  // 8x8 sub-blocks
-  constexpr int B_SUB = BT ? BN * kBK / 64 : 0;
   static_assert(AT || A_CHUNKS % 256 == 0, "tile/thread mismatch");
   static_assert(BT || B_CHUNKS % 256 == 0, "tile/thread mismatch");
-  // transposed operands: when both are transposed, threads 0..127 load A and
-  // 128..255 load B; otherwise all threads share the one transposed operand.
-  constexpr bool SPLIT_T = AT && BT;
-  constexpr int T_THREADS = SPLIT_T ? 128 : 256;
-  constexpr int A_TR = AT ? (A_SUB + T_THREADS - 1) / T_THREADS : 0;
-  constexpr int B_TR = BT ? (B_SUB + T_THREADS - 1) / T_THREADS : 0;
+  constexpr int A_SUB = AT ? BM * kBK / 64 : 0;  // 8x8 blocks of a transposed tile
+  constexpr int B_SUB = BT ? BN * kBK / 64 : 0;
+  constexpr int A_TR = (A_SUB + 255) / 256;
+  constexpr int B_TR = (B_SUB + 255) / 256;
+  constexpr int STAGE = A_CHUNKS + B_CHUNKS;
+  // bytes the epilogue stages: a [BM][BN] bf16 tile, or [BM][2*BN] for dH
+  constexpr int STG_BYTES = EPI == EPI_SWIGLU_BWD ? BM * BN * 4 : BM * BN * 2;
+  constexpr int LDS_CHUNKS = (SWAP && STG_BYTES > 2 * STAGE * 16) ? STG_BYTES / 16 : 2 * STAGE;
+  static_assert(LDS_CHUNKS * 16 <= 160 * 1024, "LDS budget of one workgroup");
 
-  __shared__ u32x4_t lds[2][A_CHUNKS + B_CHUNKS];
+  __shared__ u32x4_t lds[LDS_CHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,8 +297,9 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
     kdim = p.K;
   } else {
     const int per_e = p.m_tiles * p.n_tiles;
-    e = bid / per_e;
-    const int r = bid - e * per_e;
+    const int slot = bid / per_e;
+    e = p.order ? p.order[slot] : slot;
+    const int r = bid - slot * per_e;
     const int mt = r / p.n_tiles;
     n_tile = r - mt * p.n_tiles;
     const int row0 = p.offsets[e];
@@ -128,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
     Bb = p.B + (int64_t)row0 * p.ldb;
   }
 
-  // Global row (or column, for transposed B) of B-tile row r.
+  // Global row of B-tile row r (k-contiguous B), -1 when past the end.
   auto b_row = [&](int r) -> int {
     if (EPI == EPI_SWIGLU_FWD) {
       const int wcol = r / WN, q = r % WN;
@@ -144,9 +328,9 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
   u32x4_t rb[B_NL > 0 ? B_NL : 1];
   u32x4_t ta[A_TR > 0 ? A_TR : 1][8];
   u32x4_t tb[B_TR > 0 ? B_TR : 1][8];
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
   auto load_tiles = [&](int k0) {
-    // --- A ---
     if (!AT) {
 #pragma unroll
       for (int i = 0; i < A_NL; ++i) {
@@ -156,57 +340,45 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
         ra[i] = ld16(Ab + (int64_t)rr * p.lda + k0 + ch * 8);
       }
     } else {
-      const int t2 = SPLIT_T ? tid : tid;
 #pragma unroll
       for (int i = 0; i < A_TR; ++i) {
-        const int sidx = i * T_THREADS + t2;
+        const int sidx = i * 256 + tid;
         const int xb = sidx % (BM / 8), kb = sidx / (BM / 8);
-        const bool on = (!SPLIT_T || tid < 128) && sidx < A_SUB && (xb * 8 < m_valid);
+        const bool on = sidx < A_SUB && xb * 8 < m_valid;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int kk = k0 + kb * 8 + q;
-          if (on && kk < kdim)
-            ta[i][q] = ld16(Ab + (int64_t)kk * p.lda + m0 + xb * 8);
-          else
-            ta[i][q] = u32x4_t{0u, 0u, 0u, 0u};
+          ta[i][q] = (on && kk < kdim) ? ld16(Ab + (int64_t)kk * p.lda + m0 + xb * 8) : zero4;
         }
       }
     }
-    // --- B ---
     if (!BT) {
 #pragma unroll
       for (int i = 0; i < B_NL; ++i) {
         const int c = i * 256 + tid;
         const int r = c >> 3, ch = c & 7;
         const int g = b_row(r);
-        if (g >= 0)
-          rb[i] = ld16(Bb + (int64_t)g * p.ldb + k0 + ch * 8);
-        else
-          rb[i] = u32x4_t{0u, 0u, 0u, 0u};
+        rb[i] = g >= 0 ? ld16(Bb + (int64_t)g * p.ldb + k0 + ch * 8) : zero4;
       }
     } else {
-      const int t2 = SPLIT_T ? tid - 128 : tid;
 #pragma unroll
       for (int i = 0; i < B_TR; ++i) {
-        const int sidx = i * T_THREADS + t2;
+        const int sidx = i * 256 + tid;
         const int xb = sidx % (BN / 8), kb = sidx / (BN / 8);
         const int n = n_tile * BN + xb * 8;
-        const bool on = (!SPLIT_T || tid >= 128) && sidx >= 0 && sidx < B_SUB && n < p.N;
+        const bool on = sidx < B_SUB && n < p.N;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int kk = k0 + kb * 8 + q;
-          if (on && kk < kdim)
-            tb[i][q] = ld16(Bb + (int64_t)kk * p.ldb + n);
-          else
-            tb[i][q] = u32x4_t{0u, 0u, 0u, 0u};
+          tb[i][q] = (on && kk < kdim) ? ld16(Bb + (int64_t)kk * p.ldb + n) : zero4;
         }
       }
     }
   };
 
   auto store_tiles = [&](int buf) {
-    u32x4_t *As = lds[buf];
-    u32x4_t *Bs = lds[buf] + A_CHUNKS;
+    u32x4_t *As = lds + buf * STAGE;
+    u32x4_t *Bs = As + A_CHUNKS;
     if (!AT) {
 #pragma unroll
       for (int i = 0; i < A_NL; ++i) {
@@ -217,9 +389,8 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < A_TR; ++i) {
-        const int sidx = i * T_THREADS + (SPLIT_T ? tid : tid);
-        const bool on = (!SPLIT_T || tid < 128) && sidx < A_SUB;
-        if (on) {
+        const int sidx = i * 256 + tid;
+        if (sidx < A_SUB) {
           const int xb = sidx % (BM / 8), kb = sidx / (BM / 8);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -242,9 +413,8 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < B_TR; ++i) {
-        const int sidx = i * T_THREADS + (SPLIT_T ? tid - 128 : tid);
-        const bool on = (!SPLIT_T || tid >= 128) && sidx >= 0 && sidx < B_SUB;
-        if (on) {
+        const int sidx = i * 256 + tid;
+        if (sidx < B_SUB) {
           const int xb = sidx % (BN / 8), kb = sidx / (BN / 8);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -277,8 +447,8 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_tiles((kt + 1) * kBK);
-    const u32x4_t *As = lds[cur];
-    const u32x4_t *Bs = lds[cur] + A_CHUNKS;
+    const u32x4_t *As = lds + cur * STAGE;
+    const u32x4_t *Bs = As + A_CHUNKS;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int ch = ks * 2 + lhi;
@@ -296,92 +466,336 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) {
+          if (SWAP)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
     }
     if (kt + 1 < nk) store_tiles(cur ^ 1);
     __syncthreads();
   }
 
-  // ---------------- epilogue ----------------
-  // acc[i][j][v] sits at tile row wm*WM + i*32 + 8*(v/4) + 4*lhi + (v%4),
-  // tile column wn*WN + j*32 + l32.
-  if (EPI == EPI_SWIGLU_FWD) {
-    bf16_t *H = (bf16_t *)p.C;
-    bf16_t *Aout = p.C2;
+  epilogue<BM, BN, WM, WN, EPI>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
+}
+
+// ---------------------------------------------------------------------------
+// Forward products (both operands k-contiguous): LDS stages filled by the
+// gfx950 LDS DMA (global_load_lds_dwordx4), so that no tile data passes
+// through registers. Each stage is 64 deep in k, so every tile row of a stage
+// is one full 128-byte line and the L1 issues half as many L2 requests as
+// with 64-byte rows: the per-CU limit on outstanding requests, not the
+// matrix cores, bounds these products.
+// ---------------------------------------------------------------------------
+
+// 16 bytes per lane from global `g` into LDS at the wave-uniform byte address
+// `lds_addr` + 16 * lane. Issued from asm so that the compiler adds no waits
+// of its own; completion is awaited explicitly (s_waitcnt vmcnt) before the
+// workgroup barrier that publishes a stage. The instruction has no register
+// results, so nothing is left in flight in a register.
+MOE_DEVICE void dma16(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+}
+
+template <int N>
+MOE_DEVICE void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+MOE_DEVICE void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+constexpr int kDmaBK = 64;  // k per stage
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive 16-bit elements of row s/4;
+// lane j receives element j%4 of the rows loaded by lanes j/4 + 4q, q = 0..3.
+// With row s/4 = k and columns 4*(s%4).. this hands every lane 4 consecutive
+// k values of one column.
+MOE_DEVICE i16x4_t lds_read_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t *)(p));
+}
+
+// One operand's tile in an LDS stage, filled by DMA.
+//  KM = false: the source is k-contiguous (rows = m or n). The tile is
+//    [ROWS][64] bf16 in 128-byte rows; chunk c of row r sits at c ^ swz(r).
+//  KM = true:  the source is k-major (rows = k, contiguous along m or n).
+//    The tile is [64][ROWS] bf16; chunk c of row k sits at c ^ 4*(k % 4),
+//    which keeps the transposing fragment reads free of bank conflicts.
+// Every DMA instruction of a wave writes 1 KB of contiguous LDS.
+template <int ROWS, bool KM, int NW>
+struct Operand {
+  static constexpr int NT = NW * 64;
+  static constexpr int BYTES = ROWS * kDmaBK * 2;
+  static constexpr int NDMA = BYTES / (NT * 16);
+  static_assert(NDMA * NT * 16 == BYTES, "tile/thread mismatch");
+  static constexpr int ROWB = KM ? ROWS * 2 : 128;  // bytes per LDS tile row
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per LDS row
+  static constexpr int RPI = 1024 / ROWB;           // LDS rows per DMA instruction
+  static_assert(!KM || CPR >= 16, "k-major tiles need at least 128 columns");
+
+  const bf16_t *ptr[NDMA];  // KC: source at k = 0; KM: column base of the lane
+  int krow[NDMA];           // KM: k row of the lane within a stage
+
+  // base: first element of the tile's first row (KC) or of column 0 at k = 0
+  // (KM); ld: row pitch; valid: rows (KC) or columns (KM) that exist;
+  // row_map(r) (KC only) gives the source row of tile row r.
+  template <typename RowMap>
+  MOE_DEVICE void init(const bf16_t *base, int64_t ld, int valid, int wave, int lane, RowMap row_map) {
 #pragma unroll
-    for (int j = 0; j < FN / 2; ++j) {
-      const int g = n_tile * (BN / 2) + wn * (WN / 2) + j * 32 + l32;
-      if (g >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (r < m_valid) {
-            const float gt = acc[i][j][v];
-            const float up = acc[i][j + FN / 2][v];
-            const int64_t row = crow0 + r;
-            H[row * p.ldc + g] = f2bf(gt);
-            H[row * p.ldc + p.F + g] = f2bf(up);
-            Aout[row * p.F + g] = f2bf(silu_f(gt) * up);
-          }
-        }
-    }
-  } else if (EPI == EPI_SWIGLU_BWD) {
-    bf16_t *dH = (bf16_t *)p.C;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n_tile * BN + wn * WN + j * 32 + l32;
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (r < m_valid) {
-            const int64_t row = crow0 + r;
-            const float da = acc[i][j][v];
-            const float hg = bf2f(p.H[row * p.ldc + n]);
-            const float hu = bf2f(p.H[row * p.ldc + p.F + n]);
-            const float sg = sigmoid_f(hg);
-            dH[row * p.ldc + n] = f2bf(da * hu * sg * (1.f + hg * (1.f - sg)));
-            dH[row * p.ldc + p.F + n] = f2bf(da * hg * sg);
-          }
-        }
-    }
-  } else if (EPI == EPI_STORE) {
-    bf16_t *C = (bf16_t *)p.C;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n_tile * BN + wn * WN + j * 32 + l32;
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (r < m_valid) C[(crow0 + r) * p.ldc + n] = f2bf(acc[i][j][v]);
-        }
-    }
-  } else {  // EPI_ACC_F32
-    float *C = (float *)p.C + (int64_t)e * p.strideC;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n_tile * BN + wn * WN + j * 32 + l32;
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (r < m_valid) {
-            float *dst = C + (int64_t)(m0 + r) * p.ldc + n;
-            *dst = *dst + acc[i][j][v];
-          }
-        }
+    for (int i = 0; i < NDMA; ++i) {
+      const int r = (i * NW + wave) * RPI + lane / CPR;
+      const int phys = lane % CPR;
+      if (!KM) {
+        const int c = phys ^ swz(r);
+        ptr[i] = base + (int64_t)row_map(r) * ld + c * 8;
+        krow[i] = 0;
+      } else {
+        const int c = phys ^ (4 * (r & 3));
+        int col = c * 8;
+        if (col >= valid) col = valid - 8;  // past-the-end columns feed masked outputs only
+        ptr[i] = base + col;
+        krow[i] = r;
+      }
     }
   }
+  // Issue the DMA of stage data at k0 into LDS byte address `dst` (+ wave's
+  // 1 KB slices). KM sources clamp k rows to kdim-1; the tail is zeroed later.
+  MOE_DEVICE void issue(int k0, int64_t ld, int kdim, uint32_t dst, int wave) const {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const uint32_t d = dst + (uint32_t)((i * NW + wave) * 1024);
+      if (!KM) {
+        dma16(ptr[i] + k0, d);
+      } else {
+        int kk = k0 + krow[i];
+        if (kk >= kdim) kk = kdim - 1;
+        dma16(ptr[i] + (int64_t)kk * ld, d);
+      }
+    }
+  }
+  // 16-deep MFMA fragment of tile rows [rb, rb+32) (KC) or columns
+  // [rb, rb+32) (KM) for step ks; `tile` points at the tile in LDS.
+  MOE_DEVICE bf16x8_t frag(const char *tile, int rb, int ks, int lane) const {
+    if (!KM) {
+      const int r = rb + (lane & 31);
+      const int c = ks * 2 + (lane >> 5);
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(tile + (r * 8 + (c ^ swz(r))) * 16));
+    } else {
+      const int b = lane & 15, g = lane >> 4;
+      const int col = rb + 16 * (g & 1) + 4 * (b & 3);
+      const int chunk = col >> 3, half = (col >> 2) & 1;
+      const int k_lo = ks * 16 + 8 * (g >> 1) + (b >> 2);
+      const int phys = chunk ^ (4 * (b >> 2));  // (k_lo + 4*rd) % 4 == b >> 2
+      const char *a0 = tile + k_lo * ROWB + phys * 16 + half * 8;
+      const i16x4_t lo = lds_read_tr16(a0);
+      const i16x4_t hi = lds_read_tr16(a0 + 4 * ROWB);
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
+      const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
+
+// Grouped GEMM with DMA-fed LDS stages: 2 slots of 64-deep k, the next
+// stage in flight while the current one is consumed. A and B are each either
+// k-contiguous or k-major (transposed in the fragment reads). Ragged M
+// (forward, dgrad) or ragged K (wgrad) over experts.
+template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K>
+__global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int WAVES_N = BN / WN;
+  constexpr int WAVES_M = BM / WM;
+  static_assert(WAVES_M * WAVES_N == NW, "wavefront grid must cover the tile");
+  constexpr int FM = WM / 32, FN = WN / 32;
+  static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
+  static_assert(RAGGED_K == (EPI == EPI_ACC_F32), "weight gradients are the ragged-K products");
+  constexpr bool SWAP = EPI != EPI_ACC_F32;
+  using OpA = Operand<BM, AKM, NW>;
+  using OpB = Operand<BN, BKM, NW>;
+  constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
+  constexpr int RING_BYTES = 2 * STAGE_BYTES;
+  constexpr int STG_BYTES = !SWAP ? 0 : (EPI == EPI_SWIGLU_BWD ? BM * BN * 4 : BM * BN * 2);
+  constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+  __shared__ u32x4_t lds[LDS_BYTES / 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  if (bid >= p.total) return;
+
+  int e, m0, n_tile, m_valid, kdim;
+  int64_t crow0;
+  const bf16_t *Ab;
+  const bf16_t *Bb;
+  if (!RAGGED_K) {
+    n_tile = bid % p.n_tiles;
+    int mt;
+    if (!find_m_tile<BM>(p.offsets, p.E, bid / p.n_tiles, e, mt)) return;
+    const int row0 = p.offsets[e];
+    m0 = mt * BM;
+    m_valid = min(BM, p.offsets[e + 1] - row0 - m0);
+    crow0 = (int64_t)row0 + m0;
+    Ab = p.A + crow0 * p.lda;
+    Bb = p.B + (int64_t)e * p.strideB;
+    kdim = p.K;
+  } else {
+    const int per_e = p.m_tiles * p.n_tiles;
+    const int slot = bid / per_e;
+    e = p.order ? p.order[slot] : slot;
+    const int r = bid - slot * per_e;
+    const int mt = r / p.n_tiles;
+    n_tile = r - mt * p.n_tiles;
+    const int row0 = p.offsets[e];
+    kdim = p.offsets[e + 1] - row0;
+    if (kdim <= 0) return;  // empty expert: dW stays bit-identical
+    m0 = mt * BM;
+    m_valid = min(BM, p.M - m0);
+    crow0 = 0;
+    Ab = p.A + (int64_t)row0 * p.lda + m0;      // k-major: column m0 at k = 0
+    Bb = p.B + (int64_t)row0 * p.ldb;
+  }
+  const int n0 = n_tile * BN;
+
+  OpA opa;
+  OpB opb;
+  opa.init(Ab, p.lda, m_valid, wave, lane, [&](int r) { return r < m_valid ? r : m_valid - 1; });
+  if (EPI == EPI_SWIGLU_FWD) {
+    // B rows of the tile interleave gate and up rows per wavefront column
+    opb.init(Bb, p.ldb, p.N, wave, lane, [&](int r) {
+      const int wcol = r / WN, q = r % WN;
+      const int gi = n_tile * (BN / 2) + wcol * (WN / 2) + (q % (WN / 2));
+      const int gc = gi < p.N ? gi : p.N - 1;  // past-the-end columns are masked on output
+      return q < WN / 2 ? gc : p.F + gc;
+    });
+  } else if (!BKM) {
+    opb.init(Bb + (int64_t)n0 * p.ldb, p.ldb, p.N - n0, wave, lane,
+             [&](int r) { return r < p.N - n0 ? r : p.N - n0 - 1; });
+  } else {
+    opb.init(Bb + n0, p.ldb, p.N - n0, wave, lane, [&](int r) { return r; });
+  }
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int kt) {
+    const uint32_t sb = lds0 + (uint32_t)((kt & 1) * STAGE_BYTES);
+    const int k0 = kt * kDmaBK;
+    opa.issue(k0, p.lda, kdim, sb, wave_u);
+    opb.issue(k0, p.ldb, kdim, sb + OpA::BYTES, wave_u);
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = (kdim + kDmaBK - 1) / kDmaBK;
+  constexpr int KS = kDmaBK / 16;
+  bf16x8_t af[2][FM], bfr[2][FN];
+  // ragged K: the last stage's rows past kdim are zeroed in the A fragments
+  auto load_frags = [&](int stage, int ks, int set, bool tail) {
+    const char *sa = reinterpret_cast<const char *>(lds) + (stage & 1) * STAGE_BYTES;
+    const char *sb = sa + OpA::BYTES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[set][i] = opa.frag(sa, wm * WM + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[set][j] = opb.frag(sb, wn * WN + j * 32, ks, lane);
+    if (RAGGED_K && tail) {
+      const int kbase = stage * kDmaBK + ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (kbase + q >= kdim) af[set][i][q] = (__bf16)0.0f;
+    }
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (SWAP)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
+      }
+  };
+  // Issue order inside each step: one MFMA, one LDS read, ... so that the
+  // reads for the next step land while MFMAs run.
+  constexpr int NREAD = FM * (AKM ? 2 : 1) + FN * (BKM ? 2 : 1);
+  constexpr int NMFMA = FM * FN;
+  auto interleave = [&]() {
+    constexpr int PAIRS = NREAD < NMFMA ? NREAD : NMFMA;
+#pragma unroll
+    for (int q = 0; q < PAIRS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    if (NMFMA > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - PAIRS, 0);
+    if (NREAD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - PAIRS, 0);
+  };
+
+  // Stage kt+1 is in flight while stage kt is consumed. The barrier of
+  // iteration kt sits before its last step: every wave has then read all of
+  // stage kt (waited with lgkmcnt) and stage kt+1 has landed, so stage kt+2
+  // can be issued into the slot of stage kt.
+  constexpr int PER_STAGE = OpA::NDMA + OpB::NDMA;
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 1) wait_vm<PER_STAGE>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  load_frags(0, 0, 0, nk == 1);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool tail = kt == nk - 1;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      mfmas(ks & 1);
+      load_frags(kt, ks + 1, (ks + 1) & 1, tail);
+      interleave();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lds();
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) issue(kt + 2);
+    mfmas((KS - 1) & 1);
+    // step 0 of stage kt+1 (on the last pass a harmless read of a stale slot,
+    // kept unconditional so that it interleaves with the MFMAs above)
+    load_frags(kt + 1, 0, 0, kt + 1 == nk - 1);
+    interleave();
+  }
+  __syncthreads();  // every wave is done with the ring before it is reused
+  epilogue<BM, BN, WM, WN, EPI, NT>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
+}
+
+// Experts sorted by descending row count (ties by id), so that the longest
+// weight-gradient reductions start first. One workgroup, E <= 256.
+__global__ __launch_bounds__(256) void expert_order_kernel(const int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ order, int E) {
+  __shared__ int cnt[256];
+  const int e = threadIdx.x;
+  if (e < E) cnt[e] = offsets[e + 1] - offsets[e];
+  __syncthreads();
+  if (e >= E) return;
+  const int c = cnt[e];
+  int rank = 0;
+  for (int o = 0; o < E; ++o) {
+    const int co = cnt[o];
+    rank += (co > c) || (co == c && o < e);
+  }
+  order[rank] = e;
 }
 
 // ---------------------------------------------------------------------------
@@ -392,6 +806,15 @@ static hipError_t run_gemm(GemmParams p, hipStream_t s) {
   if (p.total <= 0) return hipSuccess;
   const int grid = (p.total + 7) / 8 * 8;
   gg_bf16_kernel<BM, BN, WM, WN, AT, BT, EPI, RAGGED_K><<<dim3((unsigned)grid), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, bool AKM, bool BKM, int EPI, bool RAGGED_K>
+static hipError_t run_dma(GemmParams p, hipStream_t s) {
+  if (p.total <= 0) return hipSuccess;
+  constexpr int NW = (BM / WM) * (BN / WN);
+  const int grid = (p.total + 7) / 8 * 8;
+  gg_dma_kernel<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K><<<dim3((unsigned)grid), NW * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -409,11 +832,10 @@ static int ragged_m_total(int64_t R, int E, int BM, int n_tiles) {
   return (int)((R / BM + E) * (int64_t)n_tiles);
 }
 
-constexpr int kBM = kGemmBM, kBN = kGemmBN, kWM = 64, kWN = 64;
-
 hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
   hipError_t err;
   {
+    constexpr int BM = kGemmBM, BN = kGemmBN;
     LaunchScope scope("gg_gateup_fwd", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.x_perm;
@@ -426,12 +848,13 @@ hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
     p.ldb = a.d;
     p.ldc = 2 * (int64_t)a.F;
     p.strideB = 2 * (int64_t)a.F * a.d;
-    p.n_tiles = (a.F + kBN / 2 - 1) / (kBN / 2);
-    p.total = ragged_m_total(a.R, a.E, kBM, p.n_tiles);
-    err = run_gemm<kBM, kBN, kWM, kWN, false, false, EPI_SWIGLU_FWD, false>(p, s);
+    p.n_tiles = (a.F + BN / 2 - 1) / (BN / 2);
+    p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
+    err = run_dma<BM, BN, BM / 2, BN / 4, false, false, EPI_SWIGLU_FWD, false>(p, s);
   }
   if (err != hipSuccess) return err;
   {
+    constexpr int BM = kGemmBM, BN = kGemmBN;
     LaunchScope scope("gg_down_fwd", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.a;
@@ -443,9 +866,9 @@ hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
     p.ldb = a.F;
     p.ldc = a.d;
     p.strideB = (int64_t)a.d * a.F;
-    p.n_tiles = (a.d + kBN - 1) / kBN;
-    p.total = ragged_m_total(a.R, a.E, kBM, p.n_tiles);
-    err = run_gemm<kBM, kBN, kWM, kWN, false, false, EPI_STORE, false>(p, s);
+    p.n_tiles = (a.d + BN - 1) / BN;
+    p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
+    err = run_dma<BM, BN, BM / 2, BN / 4, false, false, EPI_STORE, false>(p, s);
   }
   return err;
 }
@@ -453,6 +876,7 @@ hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
 hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
   hipError_t err;
   {  // B3: dA = dY W_down[e], SwiGLU backward in the epilogue -> dH
+    constexpr int BM = kGemmBM, BN = kGemmBN / 2;
     LaunchScope scope("gg_down_dgrad", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.dy;
@@ -465,30 +889,39 @@ hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
     p.ldb = a.F;
     p.ldc = 2 * (int64_t)a.F;
     p.strideB = (int64_t)a.d * a.F;
-    p.n_tiles = (a.F + kBN - 1) / kBN;
-    p.total = ragged_m_total(a.R, a.E, kBM, p.n_tiles);
-    err = run_gemm<kBM, kBN, kWM, kWN, false, true, EPI_SWIGLU_BWD, false>(p, s);
+    p.n_tiles = (a.F + BN - 1) / BN;
+    p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
+    err = run_dma<BM, BN, BM / 4, BN / 2, false, true, EPI_SWIGLU_BWD, false>(p, s);
+  }
+  if (err != hipSuccess) return err;
+  {
+    LaunchScope scope("expert_order", s);
+    expert_order_kernel<<<1, 256, 0, s>>>(a.offsets, a.order, a.E);
+    err = hipGetLastError();
   }
   if (err != hipSuccess) return err;
   {  // B4: dW_down[e] += dY_e^T a_e
+    constexpr int BM = kGemmBM, BN = kGemmBN;
     LaunchScope scope("gg_down_wgrad", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.dy;
     p.B = (const bf16_t *)a.a;
     p.C = a.dw_down;
+    p.order = a.order;
     p.M = a.d;
     p.N = a.F;
     p.lda = a.d;
     p.ldb = a.F;
     p.ldc = a.F;
     p.strideC = (int64_t)a.d * a.F;
-    p.m_tiles = (a.d + kBM - 1) / kBM;
-    p.n_tiles = (a.F + kBN - 1) / kBN;
+    p.m_tiles = (a.d + BM - 1) / BM;
+    p.n_tiles = (a.F + BN - 1) / BN;
     p.total = a.E * p.m_tiles * p.n_tiles;
-    err = run_gemm<kBM, kBN, kWM, kWN, true, true, EPI_ACC_F32, true>(p, s);
+    err = run_dma<BM, BN, BM / 2, BN / 4, true, true, EPI_ACC_F32, true>(p, s);
   }
   if (err != hipSuccess) return err;
   {  // B5: dX_perm = dH W_gu[e]
+    constexpr int BM = kGemmBM, BN = kGemmBN;
     LaunchScope scope("gg_gateup_dgrad", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.dh;
@@ -500,27 +933,29 @@ hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
     p.ldb = a.d;
     p.ldc = a.d;
     p.strideB = 2 * (int64_t)a.F * a.d;
-    p.n_tiles = (a.d + kBN - 1) / kBN;
-    p.total = ragged_m_total(a.R, a.E, kBM, p.n_tiles);
-    err = run_gemm<kBM, kBN, kWM, kWN, false, true, EPI_STORE, false>(p, s);
+    p.n_tiles = (a.d + BN - 1) / BN;
+    p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
+    err = run_dma<BM, BN, BM / 2, BN / 4, false, true, EPI_STORE, false>(p, s);
   }
   if (err != hipSuccess) return err;
   {  // B6: dW_gu[e] += dH^T X_e
+    constexpr int BM = kGemmBM, BN = kGemmBN;
     LaunchScope scope("gg_gateup_wgrad", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.dh;
     p.B = (const bf16_t *)a.x_perm;
     p.C = a.dw_gu;
+    p.order = a.order;
     p.M = 2 * a.F;
     p.N = a.d;
     p.lda = 2 * (int64_t)a.F;
     p.ldb = a.d;
     p.ldc = a.d;
     p.strideC = 2 * (int64_t)a.F * a.d;
-    p.m_tiles = (2 * a.F + kBM - 1) / kBM;
-    p.n_tiles = (a.d + kBN - 1) / kBN;
+    p.m_tiles = (2 * a.F + BM - 1) / BM;
+    p.n_tiles = (a.d + BN - 1) / BN;
     p.total = a.E * p.m_tiles * p.n_tiles;
-    err = run_gemm<kBM, kBN, kWM, kWN, true, true, EPI_ACC_F32, true>(p, s);
+    err = run_dma<BM, BN, BM / 2, BN / 4, true, true, EPI_ACC_F32, true>(p, s);
   }
   return err;
 }

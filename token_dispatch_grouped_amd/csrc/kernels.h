@@ -74,6 +74,7 @@ struct GroupedFfnArgs {
   // backward
   const void *dy;       // [R, d]
   void *dh;             // [R, 2F] (workspace)
+  int32_t *order;       // [E] experts by descending row count (workspace)
   void *dx_perm;        // [R, d]
   float *dw_gu;         // [E, 2F, d]
   float *dw_down;       // [E, d, F]

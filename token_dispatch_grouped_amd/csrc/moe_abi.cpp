@@ -14,7 +14,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.h"
 #include "validate.h"
 
@@ -322,6 +322,7 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
   fa.dw_gu = dw_gu;
   fa.dw_down = dw_down;
   fa.dh = ws;
+  fa.order = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + w.gemm_bwd_dh);
   hipStream_t hs = as_stream(stream);
   return hip_status(s.dtype == MOE_DTYPE_BF16 ? launch_ffn_bwd_bf16(fa, hs) : launch_ffn_bwd_f32(fa, hs),
                     "grouped_gemm_bwd");

@@ -60,7 +60,8 @@ WorkspaceLayout workspace_layout(const moe_shape &s) {
   w.gemm_fwd_total = 0;
   const size_t es = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
   w.gemm_bwd_dh = align256((size_t)s.T * (size_t)s.k * 2 * (size_t)s.F * es);
-  w.gemm_bwd_total = w.gemm_bwd_dh;
+  w.gemm_bwd_order = align256((size_t)s.E * 4);
+  w.gemm_bwd_total = w.gemm_bwd_dh + w.gemm_bwd_order;
   return w;
 }
 

@@ -7,15 +7,15 @@
 
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
 // Tile sizes the launchers use; validation checks that grids fit.
 constexpr int kRouteTokens = 256;       // tokens per top-k workgroup
 constexpr int kRouterChunksMax = 32;    // router weight-gradient partial sums
-constexpr int kGemmBM = 128;            // bf16 grouped GEMM rows per tile
-constexpr int kGemmBN = 128;            // bf16 grouped GEMM columns per tile
+constexpr int kGemmBM = 256;            // bf16 grouped GEMM rows per tile
+constexpr int kGemmBN = 256;            // bf16 grouped GEMM columns per tile
 constexpr int kGemmF32Tile = 16;        // fp32 grouped GEMM tile edge
 
 struct WorkspaceLayout {
@@ -24,6 +24,7 @@ struct WorkspaceLayout {
   size_t route_total;
   size_t gemm_fwd_total;
   size_t gemm_bwd_dh;     // bytes of dH
+  size_t gemm_bwd_order;  // bytes of the expert order (int32 [E])
   size_t gemm_bwd_total;
 };
 
