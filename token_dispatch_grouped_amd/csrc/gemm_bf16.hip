@@ -71,6 +71,22 @@ MOE_DEVICE uint32_t pick_pair(uint32_t a, uint32_t b, int odd) {
   return odd ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
 }
 
+// 16 bytes per lane from global `g` into LDS at the wave-uniform byte address
+// `lds_addr` + 16 * lane. Issued from asm so that the compiler adds no waits
+// of its own; completion is awaited explicitly (s_waitcnt vmcnt) before the
+// workgroup barrier that publishes a stage. The instruction has no register
+// results, so nothing is left in flight in a register.
+MOE_DEVICE void dma16(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+}
+
+template <int N>
+MOE_DEVICE void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+MOE_DEVICE void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Epilogue shared by the grouped GEMM kernels. With EPI_ACC_F32 the
 // accumulators are in MFMA order (lane = column); otherwise in swapped order
 // (lane = row, four consecutive columns per accumulator group) and `lds`
@@ -86,22 +102,33 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   if (EPI == EPI_ACC_F32) {
     // acc[i][j][v] sits at tile row wm*WM + i*32 + 8*(v/4) + 4*lhi + (v%4),
-    // tile column wn*WN + j*32 + l32.
+    // tile column wn*WN + j*32 + l32. The 16 old values of a fragment are
+    // loaded together (clamped addresses, so no load waits on a branch),
+    // then the valid ones are written back.
     float *C = (float *)p.C + (int64_t)e * p.strideC;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n_tile * BN + wn * WN + j * 32 + l32;
-      if (n >= p.N) continue;
+    for (int i = 0; i < FM; ++i) {
+      float old[FN][16];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j) {
+        const int n = n_tile * BN + wn * WN + j * 32 + l32;
+        const int nn = n < p.N ? n : p.N - 1;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (r < m_valid) {
-            float *dst = C + (int64_t)(m0 + r) * p.ldc + n;
-            *dst = *dst + acc[i][j][v];
-          }
+          const int rr = r < m_valid ? r : m_valid - 1;
+          old[j][v] = C[(int64_t)(m0 + rr) * p.ldc + nn];
         }
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n_tile * BN + wn * WN + j * 32 + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
+          if (r < m_valid && n < p.N) C[(int64_t)(m0 + r) * p.ldc + n] = old[j][v] + acc[i][j][v];
+        }
+      }
     }
     return;
   }
@@ -191,15 +218,28 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
   } else {  // EPI_SWIGLU_BWD: stage h (gate | up) in LDS, rewrite it as dH
     constexpr int SW = 2 * BN;
     const int n0 = n_tile * BN;
-    constexpr int cpr = SW / 8;
-    for (int c = tid; c < BM * cpr; c += NT) {
-      const int r = c / cpr, ch = c - r * cpr;
+    // The h tile arrives by LDS DMA: each wave instruction fills 1 KB, i.e.
+    // 1024/(2*SW) staged rows; lane l takes physical chunk l % (SW/8) of its
+    // row, which holds logical chunk phys ^ (row & 15). Rows past m_valid and
+    // columns past N are clamped (their results are never stored).
+    constexpr int CPR = SW / 8;
+    constexpr int RPI = 1024 / (SW * 2);
+    constexpr int NI = BM * SW * 2 / (NT * 16);
+    static_assert(NI * NT * 16 == BM * SW * 2, "h tile/thread mismatch");
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int r = (q * (NT / 64) + wv) * RPI + lane / CPR;
+      const int ch = (lane % CPR) ^ (r & 15);
       const int col = ch * 8;
-      const int gcol = col < BN ? n0 + col : n0 + col - BN;
-      u32x4_t v = zero4;
-      if (r < m_valid && gcol < p.N) v = ld16(p.H + (crow0 + r) * p.ldc + (col < BN ? gcol : p.F + gcol));
-      *reinterpret_cast<u32x4_t *>(stg + r * SW + ((ch ^ (r & 15)) << 3)) = v;
+      int gcol = col < BN ? n0 + col : n0 + col - BN;
+      if (gcol > p.N - 8) gcol = p.N - 8;
+      const int rr = r < m_valid ? r : m_valid - 1;
+      dma16(p.H + (crow0 + rr) * p.ldc + (col < BN ? gcol : p.F + gcol),
+            lds0 + (uint32_t)((q * (NT / 64) + wv) * 1024));
     }
+    wait_vm<0>();
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -489,22 +529,6 @@ __global__ __launch_bounds__(256, 1) void gg_bf16_kernel(GemmParams p) {
 // matrix cores, bounds these products.
 // ---------------------------------------------------------------------------
 
-// 16 bytes per lane from global `g` into LDS at the wave-uniform byte address
-// `lds_addr` + 16 * lane. Issued from asm so that the compiler adds no waits
-// of its own; completion is awaited explicitly (s_waitcnt vmcnt) before the
-// workgroup barrier that publishes a stage. The instruction has no register
-// results, so nothing is left in flight in a register.
-MOE_DEVICE void dma16(const void *g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
-}
-
-template <int N>
-MOE_DEVICE void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-MOE_DEVICE void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 constexpr int kDmaBK = 64;  // k per stage
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
@@ -628,7 +652,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bid = RAGGED_K ? xcd_run_remap(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
   if (bid >= p.total) return;
 
   int e, m0, n_tile, m_valid, kdim;
@@ -813,7 +837,7 @@ template <int BM, int BN, int WM, int WN, bool AKM, bool BKM, int EPI, bool RAGG
 static hipError_t run_dma(GemmParams p, hipStream_t s) {
   if (p.total <= 0) return hipSuccess;
   constexpr int NW = (BM / WM) * (BN / WN);
-  const int grid = (p.total + 7) / 8 * 8;
+  const int grid = RAGGED_K ? (p.total + 63) / 64 * 64 : (p.total + 7) / 8 * 8;
   gg_dma_kernel<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K><<<dim3((unsigned)grid), NW * 64, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -9,6 +9,15 @@ namespace moe {
 // rows) run on the same XCD: hardware hands workgroup b to XCD b % 8.
 MOE_DEVICE int xcd_remap(int bid, int grid) { return (bid & 7) * (grid >> 3) + (bid >> 3); }
 
+// Balanced variant for work of uneven cost ordered heaviest first: runs of 8
+// consecutive logical workgroups (tiles that share an operand slab) stay on
+// one XCD, and successive runs go to successive XCDs, so every XCD receives
+// its share of the heavy front of the order. The grid is a multiple of 64.
+MOE_DEVICE int xcd_run_remap(int bid) {
+  const int xcd = bid & 7, q = bid >> 3;
+  return ((((q >> 3) << 3) + xcd) << 3) + (q & 7);
+}
+
 // Ragged-M tile lookup: the mslot-th BM-row tile over all experts in order.
 // Each lane sums the tiles of four experts, a wavefront scan finds the owner.
 // Returns false when mslot is past the last tile.
