@@ -37,6 +37,40 @@ GEMM_KERNELS = {
 }
 MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 
+# HBM-side bytes per launch measured with rocprofv3 FETCH_SIZE and WRITE_SIZE
+# passes (each scaled by what the counter reads for a plain 1 GiB device copy:
+# x2.0 and x1.0), on the ep_share_32k workload. Valid only for the GEMM
+# sources they were taken on: any change to those files reports null.
+TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
+                   "token_dispatch_grouped_amd/csrc/common.h")
+TRAFFIC = {
+    "sources_sha256": "e5e3357abf8bbe3ac0d2103211c6f13662e285c37754b762515e3cba7cec3fac",
+    "workload": "ep_share_32k",
+    "bytes_per_launch": {
+        # read GiB + write GiB, x 2^30
+        "gg_gateup_fwd": (10.441 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.216 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (5.756 + 1.375) * 2 ** 30,
+        "gg_gateup_dgrad": (4.484 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (11.537 + 0.645) * 2 ** 30,
+    },
+}
+
+
+def measured_traffic(kernel, workload):
+    """Bytes per launch from the counter passes, or None when the GEMM
+    sources or the workload differ from those the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    try:
+        for f in TRAFFIC_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except OSError:
+        return None
+    if h.hexdigest() != TRAFFIC["sources_sha256"] or workload != TRAFFIC["workload"]:
+        return None
+    return TRAFFIC["bytes_per_launch"].get(kernel)
+
 
 def mem_bytes(name, T, d, k, s, router=False):
     """Algorithmic HBM bytes of one launch of a data-movement kernel."""
@@ -60,6 +94,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle's timed sample (0 disables the CPU baseline)")
     ap.add_argument("--renorm", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device copy of BYTES bytes before timing (a known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -157,6 +194,14 @@ def main():
             layer.forward(T, mb["x"], wgu, wdn, logits=mb["logits"], w_router=wr, bias=bias)
             layer.backward(T, mb["dout"], wgu, wdn, dw_gu, dw_dn, x=mb["x"], w_router=wr, dw_router=dw_r)
 
+    if args.calibrate_copy > 0:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -212,8 +257,9 @@ def main():
     if dbase in GEMM_KERNELS:
         per_launch = kernels[dom]["flops_per_launch"]
         ach = per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        tr = measured_traffic(dom, w.name)
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None,
+                "frac": round(ach / peak, 4), "traffic": None if tr is None else round(tr),
                 "work_per_launch": f"{GEMM_KERNELS[dbase]}*R*d*F = {per_launch:.4g} FLOP"}
     else:
         per_launch = sum(mem_bytes(dom, mb["T"], w.d, w.k, s, router) for mb in mbs) / max(1, kernels[dom][

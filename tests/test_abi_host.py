@@ -1,0 +1,196 @@
+"""Host-side tests of the C ABI (CPU only, no GPU needed).
+
+* the shared library loads and exports every function include/moe.h declares;
+* argument validation returns the documented status before anything is
+  launched (so these calls are safe without a GPU);
+* T == 0 is a successful no-op that accepts NULL tensors;
+* workspace sizes are monotone in T, so a workspace sized for the largest
+  microbatch serves every smaller one;
+* the validation code, built alone with g++ and AddressSanitizer, passes a
+  table of cases (host code only).
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import token_dispatch_grouped_amd as moe
+from token_dispatch_grouped_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+CSRC = os.path.join(ROOT, "token_dispatch_grouped_amd", "csrc")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    # and the binding wraps each of them
+    assert set(names) <= set(L.exported_names())
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in moe.moe_version()
+    assert moe.moe_status_string(0) == "ok"
+    assert "workspace" in moe.moe_status_string(3)
+
+
+def shape(T=64, d=64, E=4, k=2, F=128, dtype=L.MOE_DTYPE_BF16, flags=0):
+    return L.make_shape(T, d, E, k, F, dtype, flags)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=5, E=4), L.MOE_ERR_INVALID_ARGUMENT),        # k > E
+    (dict(T=-1), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(d=0), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(d=96), L.MOE_ERR_UNSUPPORTED),                 # not a multiple of 64
+    (dict(F=100), L.MOE_ERR_UNSUPPORTED),
+    (dict(E=257, k=2), L.MOE_ERR_UNSUPPORTED),
+    (dict(E=32, k=17), L.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.MOE_ERR_UNSUPPORTED),
+    (dict(flags=2), L.MOE_ERR_UNSUPPORTED),
+    (dict(T=2 ** 28, E=8, k=8), L.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
+])
+def test_shape_validation(kw, status):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(shape(**kw))
+    assert ei.value.status == status
+
+
+def test_empty_microbatch_is_a_noop_with_nulls():
+    s = shape(T=0)
+    moe.moe_route(s, None, None, None, None, None, None, None, None, None, None, None, 0, stream=0)
+    moe.moe_permute(s, None, None, None, stream=0)
+    moe.moe_grouped_gemm_fwd(s, None, None, None, None, None, None, None, None, 0, stream=0)
+    moe.moe_unpermute_combine(s, None, None, None, None, stream=0)
+    moe.moe_unpermute_combine_bwd(s, None, None, None, None, None, None, stream=0)
+    moe.moe_route_bwd(s, None, None, None, None, None, None, None, None, None, None, 0, stream=0)
+    moe.moe_grouped_gemm_bwd(s, None, None, None, None, None, None, None, None, None, None, None, 0, stream=0)
+    moe.moe_permute_bwd(s, None, None, None, None, stream=0)
+
+
+def test_empty_microbatch_still_validates_shape():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_permute(shape(T=0, k=9, E=4), None, None, None, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+
+
+FAKE = 1 << 20  # an aligned, never dereferenced address: validation fails first
+
+
+def test_null_pointer_is_rejected():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_permute(shape(), FAKE, None, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    assert "row_of_slot" in str(ei.value)
+
+
+def test_misaligned_pointer_is_rejected():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_unpermute_combine(shape(), FAKE, FAKE + 4, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_MISALIGNED
+
+
+def test_router_mode_argument_rules():
+    s = shape()
+    # logits given (no router): x must be NULL
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(s, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    # router mode without x
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(s, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    # route_bwd in router mode needs dx_router and dw_router
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_bwd(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_rules():
+    s = shape()
+    route_ws, fwd_ws, bwd_ws = moe.moe_workspace_size(s)
+    assert route_ws > 0 and bwd_ws > 0
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(s, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, route_ws - 1, stream=0)
+    assert ei.value.status == L.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_grouped_gemm_bwd(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, stream=0)
+    assert ei.value.status == L.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("dtype", [L.MOE_DTYPE_BF16, L.MOE_DTYPE_F32])
+def test_workspace_monotone_in_T(dtype):
+    prev = None
+    for T in [0, 1, 7, 255, 256, 257, 4096, 7001, 16384, 32768]:
+        ws = moe.moe_workspace_size(shape(T=T, d=2048, E=32, k=8, F=1408, dtype=dtype))
+        if prev is not None:
+            assert all(a >= b for a, b in zip(ws, prev)), (T, ws, prev)
+        prev = ws
+    # the gemm backward workspace holds dH: R * 2F elements of the layer dtype
+    R = 32768 * 8
+    es = 2 if dtype == L.MOE_DTYPE_BF16 else 4
+    assert prev[2] >= R * 2 * 1408 * es
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_validation_built_alone_with_asan(tmp_path):
+    """The validation unit is plain C++: build it with g++ (no HIP) and
+    AddressSanitizer, and check a table of cases."""
+    driver = tmp_path / "drv.cpp"
+    driver.write_text(r'''
+#include "validate.h"
+#include <cstdio>
+using namespace moe;
+static int fails = 0;
+static void expect(moe_status got, moe_status want, const char* what) {
+  if (got != want) { std::printf("FAIL %s: got %d want %d\n", what, (int)got, (int)want); ++fails; }
+}
+int main() {
+  std::string why;
+  moe_shape s{32768, 2048, 32, 8, 1408, MOE_DTYPE_BF16, 0};
+  expect(validate_shape(&s, &why), MOE_OK, "ep share");
+  expect(validate_shape(nullptr, &why), MOE_ERR_INVALID_ARGUMENT, "null shape");
+  moe_shape b = s; b.E = 64; b.k = 33; expect(validate_shape(&b, &why), MOE_ERR_UNSUPPORTED, "k>16");
+  b = s; b.k = 40; b.E = 32; expect(validate_shape(&b, &why), MOE_ERR_INVALID_ARGUMENT, "k>E");
+  b = s; b.F = 1400; expect(validate_shape(&b, &why), MOE_ERR_UNSUPPORTED, "F%64");
+  b = s; b.T = 0; expect(validate_shape(&b, &why), MOE_OK, "T=0");
+  WorkspaceLayout w = workspace_layout(s);
+  if (w.gemm_bwd_total < (size_t)32768 * 8 * 2 * 1408 * 2) { std::printf("FAIL dh size\n"); ++fails; }
+  int x = 0;
+  PtrArg ok[] = {{"a", (void*)0x1000, true, false}, {"b", nullptr, false, true}};
+  expect(validate_ptrs(ok, 2, &why), MOE_OK, "ptrs ok");
+  PtrArg mis[] = {{"a", (void*)0x1004, true, false}};
+  expect(validate_ptrs(mis, 1, &why), MOE_ERR_MISALIGNED, "misaligned");
+  PtrArg nul[] = {{"a", nullptr, true, false}};
+  expect(validate_ptrs(nul, 1, &why), MOE_ERR_INVALID_ARGUMENT, "null");
+  PtrArg must[] = {{"a", &x, false, true}};
+  expect(validate_ptrs(must, 1, &why), MOE_ERR_INVALID_ARGUMENT, "must be null");
+  expect(validate_workspace(nullptr, 0, 0, &why), MOE_OK, "no ws needed");
+  expect(validate_workspace(nullptr, 0, 16, &why), MOE_ERR_WORKSPACE, "ws null");
+  expect(validate_workspace((void*)0x1000, 8, 16, &why), MOE_ERR_WORKSPACE, "ws short");
+  std::printf("%d failures\n", fails);
+  return fails != 0;
+}
+''')
+    exe = tmp_path / "drv"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, str(driver), os.path.join(CSRC, "validate.cpp"),
+           "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failures" in r.stdout
