@@ -94,6 +94,7 @@ MOE_DEVICE void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); 
 template <int BM, int BN, int WM, int WN, int EPI, int NT = 256>
 MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32], u32x4_t *lds, int e, int m0,
                          int n_tile, int m_valid, int64_t crow0, int wm, int wn) {
+  constexpr int WAVES_M = BM / WM;
   constexpr int FM = WM / 32, FN = WN / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -215,69 +216,89 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
         }
     __syncthreads();
     flush(BN / 2, p.C2, p.F, [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
-  } else {  // EPI_SWIGLU_BWD: stage h (gate | up) in LDS, rewrite it as dH
-    constexpr int SW = 2 * BN;
+  } else {  // EPI_SWIGLU_BWD: dA -> dH = (dH_gate | dH_up) using the saved h
+    // The tile is finished in WAVES_M row bands (one band per wavefront row
+    // wm). For each band the h_gate and h_up tiles arrive by LDS DMA into two
+    // [WM][BN] staging tiles; the band's wavefronts rewrite them in place as
+    // dH_gate and dH_up; all threads then store both.
+    // DMA layout: wave instruction q fills 1 KB = 1024/(2*BN) staged rows;
+    // lane l takes physical chunk l % (BN/8) of its row, i.e. logical chunk
+    // phys ^ (row & 15). Rows past m_valid and columns past N are clamped
+    // (their results are never stored).
+    static_assert(2 * WM * BN * 2 <= 160 * 1024, "two staged bands must fit in LDS");
     const int n0 = n_tile * BN;
-    // The h tile arrives by LDS DMA: each wave instruction fills 1 KB, i.e.
-    // 1024/(2*SW) staged rows; lane l takes physical chunk l % (SW/8) of its
-    // row, which holds logical chunk phys ^ (row & 15). Rows past m_valid and
-    // columns past N are clamped (their results are never stored).
-    constexpr int CPR = SW / 8;
-    constexpr int RPI = 1024 / (SW * 2);
-    constexpr int NI = BM * SW * 2 / (NT * 16);
-    static_assert(NI * NT * 16 == BM * SW * 2, "h tile/thread mismatch");
+    constexpr int CPR = BN / 8;
+    constexpr int RPI = 1024 / (BN * 2);
+    constexpr int NI = WM * BN * 2 / (NT * 16);
+    static_assert(NI * NT * 16 == WM * BN * 2 && CPR >= 16, "h band/thread mismatch");
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    bf16_t *sg_tile = stg;                 // [WM][BN] h_gate -> dH_gate
+    bf16_t *su_tile = stg + WM * BN;       // [WM][BN] h_up   -> dH_up
+    for (int band = 0; band < WAVES_M; ++band) {
+      const int rbase = band * WM;
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int r = (q * (NT / 64) + wv) * RPI + lane / CPR;
-      const int ch = (lane % CPR) ^ (r & 15);
-      const int col = ch * 8;
-      int gcol = col < BN ? n0 + col : n0 + col - BN;
-      if (gcol > p.N - 8) gcol = p.N - 8;
-      const int rr = r < m_valid ? r : m_valid - 1;
-      dma16(p.H + (crow0 + rr) * p.ldc + (col < BN ? gcol : p.F + gcol),
-            lds0 + (uint32_t)((q * (NT / 64) + wv) * 1024));
+      for (int q = 0; q < NI; ++q) {
+        const int r = (q * (NT / 64) + wv) * RPI + lane / CPR;
+        const int ch = (lane % CPR) ^ (r & 15);
+        int gcol = n0 + ch * 8;
+        if (gcol > p.N - 8) gcol = p.N - 8;
+        int rr = rbase + r;
+        if (rr >= m_valid) rr = m_valid - 1;
+        const bf16_t *src = p.H + (crow0 + rr) * p.ldc + gcol;
+        const uint32_t off = (uint32_t)((q * (NT / 64) + wv) * 1024);
+        dma16(src, lds0 + off);
+        dma16(src + p.F, lds0 + (uint32_t)(WM * BN * 2) + off);
+      }
+      wait_vm<0>();
+      __syncthreads();
+      if (wm == band) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int r = i * 32 + l32;
+              const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
+              uint2 *pg = reinterpret_cast<uint2 *>(sg_tile + stg_off(r, col, BN));
+              uint2 *pu = reinterpret_cast<uint2 *>(su_tile + stg_off(r, col, BN));
+              const uint2 hg2 = *pg, hu2 = *pu;
+              const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
+                                   __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
+              const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
+                                   __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
+              float dg[4], du[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float da = acc[i][j][4 * g + q];
+                const float sgm = sigmoid_f(hg[q]);
+                dg[q] = da * hu[q] * sgm * (1.f + hg[q] * (1.f - sgm));
+                du[q] = da * hg[q] * sgm;
+              }
+              uint2 og, ou;
+              og.x = pack_bf2(dg[0], dg[1]);
+              og.y = pack_bf2(dg[2], dg[3]);
+              ou.x = pack_bf2(du[0], du[1]);
+              ou.y = pack_bf2(du[2], du[3]);
+              *pg = og;
+              *pu = ou;
+            }
+      }
+      __syncthreads();
+      // store the band: gate half then up half, 16 bytes per lane
+      constexpr int BCH = WM * CPR;  // chunks per staged band tile
+      for (int c = tid; c < 2 * BCH; c += NT) {
+        const int up = c >= BCH;
+        const int cc = up ? c - BCH : c;
+        const int r = cc / CPR, ch = cc - r * CPR;
+        if (rbase + r >= m_valid || n0 + ch * 8 >= p.N) continue;
+        const bf16_t *t = up ? su_tile : sg_tile;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + r * BN + ((ch ^ (r & 15)) << 3));
+        st16((bf16_t *)p.C + (crow0 + rbase + r) * p.ldc + (up ? p.F : 0) + n0 + ch * 8, v);
+      }
+      __syncthreads();
     }
-    wait_vm<0>();
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r = wm * WM + i * 32 + l32;
-          const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
-          uint2 *pg = reinterpret_cast<uint2 *>(stg + stg_off(r, col, SW));
-          uint2 *pu = reinterpret_cast<uint2 *>(stg + stg_off(r, BN + col, SW));
-          const uint2 hg2 = *pg, hu2 = *pu;
-          const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
-                               __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
-          const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
-                               __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
-          float dg[4], du[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float da = acc[i][j][4 * g + q];
-            const float sg = sigmoid_f(hg[q]);
-            dg[q] = da * hu[q] * sg * (1.f + hg[q] * (1.f - sg));
-            du[q] = da * hg[q] * sg;
-          }
-          uint2 og, ou;
-          og.x = pack_bf2(dg[0], dg[1]);
-          og.y = pack_bf2(dg[2], dg[3]);
-          ou.x = pack_bf2(du[0], du[1]);
-          ou.y = pack_bf2(du[2], du[3]);
-          *pg = og;
-          *pu = ou;
-        }
-    __syncthreads();
-    flush(SW, (bf16_t *)p.C, p.ldc, [&](int c) {
-      if (c < BN) return n0 + c < p.N ? n0 + c : -1;
-      const int n = n0 + c - BN;
-      return n < p.N ? p.F + n : -1;
-    });
   }
 }
 
@@ -530,6 +551,7 @@ __global__ __launch_bounds__(256, 1) void gg_bf16_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 
 constexpr int kDmaBK = 64;  // k per stage
+constexpr int kGroupM = 4;  // row tiles per group in the ragged-M tile order
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 
@@ -641,7 +663,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   using OpB = Operand<BN, BKM, NW>;
   constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
   constexpr int RING_BYTES = 2 * STAGE_BYTES;
-  constexpr int STG_BYTES = !SWAP ? 0 : (EPI == EPI_SWIGLU_BWD ? BM * BN * 4 : BM * BN * 2);
+  constexpr int STG_BYTES = !SWAP ? 0 : BM * BN * 2;
   constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
   __shared__ u32x4_t lds[LDS_BYTES / 16];
@@ -660,9 +682,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   const bf16_t *Ab;
   const bf16_t *Bb;
   if (!RAGGED_K) {
-    n_tile = bid % p.n_tiles;
+    // logical order: groups of kGroupM row tiles, column tile outer inside a
+    // group, so the workgroups resident on one XCD share both operands
+    const int per = kGroupM * p.n_tiles;
+    const int grp = bid / per, rem = bid - grp * per;
+    n_tile = rem / kGroupM;
+    const int mslot = grp * kGroupM + (rem - n_tile * kGroupM);
     int mt;
-    if (!find_m_tile<BM>(p.offsets, p.E, bid / p.n_tiles, e, mt)) return;
+    if (!find_m_tile<BM>(p.offsets, p.E, mslot, e, mt)) return;
     const int row0 = p.offsets[e];
     m0 = mt * BM;
     m_valid = min(BM, p.offsets[e + 1] - row0 - m0);
@@ -853,7 +880,8 @@ static GemmParams base_params(const GroupedFfnArgs &a) {
 // Ragged-M grid: an upper bound of the number of BM-row tiles over all
 // experts (sum of ceil(M_e/BM) <= R/BM + E), times the column tiles.
 static int ragged_m_total(int64_t R, int E, int BM, int n_tiles) {
-  return (int)((R / BM + E) * (int64_t)n_tiles);
+  const int64_t slots = (R / BM + E + kGroupM - 1) / kGroupM * kGroupM;
+  return (int)(slots * (int64_t)n_tiles);
 }
 
 hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
@@ -900,7 +928,7 @@ hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
 hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
   hipError_t err;
   {  // B3: dA = dY W_down[e], SwiGLU backward in the epilogue -> dH
-    constexpr int BM = kGemmBM, BN = kGemmBN / 2;
+    constexpr int BM = kGemmBM, BN = kGemmBN;
     LaunchScope scope("gg_down_dgrad", s);
     GemmParams p = base_params(a);
     p.A = (const bf16_t *)a.dy;
@@ -915,7 +943,7 @@ hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
     p.strideB = (int64_t)a.d * a.F;
     p.n_tiles = (a.F + BN - 1) / BN;
     p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
-    err = run_dma<BM, BN, BM / 4, BN / 2, false, true, EPI_SWIGLU_BWD, false>(p, s);
+    err = run_dma<BM, BN, BM / 2, BN / 4, false, true, EPI_SWIGLU_BWD, false>(p, s);
   }
   if (err != hipSuccess) return err;
   {
