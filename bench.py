@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ep_share_32k")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle's timed sample (0 disables the CPU baseline)")
     ap.add_argument("--renorm", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -130,7 +130,9 @@ def cpu_baseline(w, inp, target_s):
         oracle.layer_bwd(dout, sv, wgu, wdn, x=x, w_router=wr)
         return time.perf_counter() - t0
 
-    Ts = min(T_full, 256)
+    # size the sample from a 1024-token probe (small probes overstate the
+    # per-token cost: per-expert overheads dominate them)
+    Ts = min(T_full, 1024)
     dt = run(Ts)
     if dt < target_s and Ts < T_full:
         Ts = int(min(T_full, max(Ts, Ts * target_s / max(dt, 1e-3))))

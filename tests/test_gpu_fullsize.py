@@ -42,7 +42,7 @@ def _run_full(w, inp):
     return layer, sv, g, dw_gu, dw_dn
 
 
-@pytest.mark.parametrize("name", ["ep_share_32k", "large_share_zipf"])
+@pytest.mark.parametrize("name", ["ep_share_32k", "large_share_zipf", "large_share_uniform"])
 def test_fullsize_sampled(name):
     w = WORKLOADS[name]
     print(f"[fullsize] {name}: T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
@@ -108,3 +108,85 @@ def test_fullsize_sampled(name):
     import torch
     for t in (sv.out, sv.y, sv.h, g["dx"], g["dx_perm"], dw_gu, dw_dn):
         assert bool(torch.isfinite(t).all())
+
+
+def _expert_dw_oracle(w, mb, W, r, e):
+    """fp64 weight gradients of expert e from one microbatch, computed by the
+    oracle on that expert's own rows."""
+    k = w.k
+    lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+    wgu64, wdn64 = to_f64(W["w_gu"][e:e + 1], BF16), to_f64(W["w_down"][e:e + 1], BF16)
+    if hi == lo:
+        return np.zeros(wgu64.shape[1:]), np.zeros(wdn64.shape[1:])
+    slots = r["src_of_row"][lo:hi]
+    t_of = slots // k
+    x_e = to_f64(mb["x"], BF16)[t_of]
+    w_e = r["topk_w"].reshape(-1)[slots][:, None]
+    dout_e = to_f64(mb["dout"], BF16)[t_of]
+    off1 = np.array([0, hi - lo], dtype=np.int32)
+    h_e, a_e, y_e = oracle.expert_ffn_fwd(x_e, wgu64, wdn64, off1)
+    dy_e, _ = oracle.unpermute_combine_bwd(dout_e, y_e, w_e, np.arange(hi - lo, dtype=np.int32)[:, None])
+    _, dwgu, dwdn, _ = oracle.expert_ffn_bwd(dy_e, x_e, h_e, a_e, wgu64, wdn64, off1)
+    return dwgu[0], dwdn[0]
+
+
+def test_fullsize_microbatch_accumulation():
+    """Four microbatches T = 16384, 7001, 0, 32768 on one set of buffers sized
+    for the largest; fp32 weight gradients accumulate; the empty microbatch
+    launches nothing and leaves them bit-identical."""
+    import torch
+    import token_dispatch_grouped_amd as moe
+    from token_dispatch_grouped_amd.layer import MoeLayer
+    w = WORKLOADS["microbatches_32k"]
+    print(f"[fullsize] microbatches {w.microbatches} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
+    inp = make_inputs(w)
+    W = inp["weights"]
+    layer = MoeLayer(max(w.microbatches), w.d, w.E, w.k, w.F, moe.MOE_DTYPE_BF16)
+    wgu = to_device(W["w_gu"], BF16)
+    wdn = to_device(W["w_down"], BF16)
+    dw_gu = torch.zeros(w.E, 2 * w.F, w.d, device="cuda")
+    dw_dn = torch.zeros(w.E, w.d, w.F, device="cuda")
+    tol = TOL[BF16]
+    routes = []
+    rng = np.random.default_rng(1)
+    for i, mb in enumerate(inp["micro"]):
+        T = mb["x"].shape[0]
+        before = (dw_gu.clone(), dw_dn.clone())
+        x = to_device(mb["x"], BF16)
+        sv = layer.forward(T, x, wgu, wdn, logits=to_device(mb["logits"], F32))
+        g = layer.backward(T, to_device(mb["dout"], BF16), wgu, wdn, dw_gu, dw_dn)
+        torch.cuda.synchronize()
+        r = oracle.route(mb["logits"].astype(np.float64), w.k)
+        routes.append(r)
+        if T == 0:
+            assert torch.equal(before[0], dw_gu) and torch.equal(before[1], dw_dn)
+            continue
+        for key in ("topk_idx", "counts", "offsets", "row_of_slot", "src_of_row"):
+            assert np.array_equal(getattr(sv, key).cpu().numpy(), r[key]), (i, key)
+        toks = np.unique(np.concatenate([rng.integers(0, T, 16), [0, T - 1]]))
+        wgu64, wdn64 = to_f64(W["w_gu"], BF16), to_f64(W["w_down"], BF16)
+        out_s, sv_s = oracle.layer_fwd(to_f64(mb["x"], BF16)[toks], wgu64, wdn64, w.k,
+                                       logits=mb["logits"][toks].astype(np.float64))
+        g_s = oracle.layer_bwd(to_f64(mb["dout"], BF16)[toks], sv_s, wgu64, wdn64)
+        assert_close(f"mb{i} out", to_host64(sv.out[toks.tolist()]), out_s, tol)
+        assert_close(f"mb{i} dx", to_host64(g["dx"][toks.tolist()]), g_s["dx"], tol)
+    # accumulated gradients of one expert that is non-empty in every non-empty
+    # microbatch: the sum of the per-microbatch oracle gradients
+    live = [np.nonzero(r["counts"] > 0)[0] for r, mb in zip(routes, inp["micro"]) if mb["x"].shape[0] > 0]
+    common = sorted(set(live[0]).intersection(*map(set, live[1:])))
+    e = min(common, key=lambda ee: sum(int(r["counts"][ee]) for r in routes))
+    acc_gu = 0.0
+    acc_dn = 0.0
+    for r, mb in zip(routes, inp["micro"]):
+        if mb["x"].shape[0] == 0:
+            continue
+        a, b = _expert_dw_oracle(w, mb, W, r, e)
+        acc_gu = acc_gu + a
+        acc_dn = acc_dn + b
+    print(f"[fullsize] accumulated dW check on expert {e}", flush=True)
+    assert_close(f"dw_gu[{e}] accumulated", to_host64(dw_gu[e]), acc_gu, tol)
+    assert_close(f"dw_down[{e}] accumulated", to_host64(dw_dn[e]), acc_dn, tol)
+    # experts empty in every microbatch keep exactly zero gradients
+    for ee in range(w.E):
+        if all(int(r["counts"][ee]) == 0 for r in routes):
+            assert float(dw_gu[ee].abs().max()) == 0.0 and float(dw_dn[ee].abs().max()) == 0.0
