@@ -62,14 +62,8 @@ struct GemmParams {
   int total;              // logical workgroups
 };
 
-constexpr int kBK = 64;
-
 MOE_DEVICE int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Combine two bf16 lanes: element `odd` of dwords a and b.
-MOE_DEVICE uint32_t pick_pair(uint32_t a, uint32_t b, int odd) {
-  return odd ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
 
 // 16 bytes per lane from global `g` into LDS at the wave-uniform byte address
 // `lds_addr` + 16 * lane. Issued from asm so that the compiler adds no waits
@@ -302,256 +296,12 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool AT, bool BT, int EPI, bool RAGGED_K>
-__global__ __launch_bounds__(256, 1) void gg_bf16_kernel(GemmParams p) {
-  constexpr int WAVES_N = BN / WN;
-  constexpr int WAVES_M = BM / WM;
-  static_assert(WAVES_M * WAVES_N == 4, "4 wavefronts per workgroup");
-  constexpr int FM = WM / 32, FN = WN / 32;
-  static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
-  // bf16 epilogues use the swapped MFMA (lane = output row, 4 consecutive
-  // columns per accumulator group); the fp32 accumulate keeps lane = column.
-  constexpr bool SWAP = EPI != EPI_ACC_F32;
-  constexpr int A_CHUNKS = BM * kBK / 8;  // 16-byte chunks per operand tile
-  constexpr int B_CHUNKS = BN * kBK / 8;
-  constexpr int A_NL = AT ? 0 : A_CHUNKS / 256;
-  constexpr int B_NL = BT ? 0 : B_CHUNKS / 256;
-  static_assert(AT || A_CHUNKS % 256 == 0, "tile/thread mismatch");
-  static_assert(BT || B_CHUNKS % 256 == 0, "tile/thread mismatch");
-  constexpr int A_SUB = AT ? BM * kBK / 64 : 0;  // 8x8 blocks of a transposed tile
-  constexpr int B_SUB = BT ? BN * kBK / 64 : 0;
-  constexpr int A_TR = (A_SUB + 255) / 256;
-  constexpr int B_TR = (B_SUB + 255) / 256;
-  constexpr int STAGE = A_CHUNKS + B_CHUNKS;
-  // bytes the epilogue stages: a [BM][BN] bf16 tile, or [BM][2*BN] for dH
-  constexpr int STG_BYTES = EPI == EPI_SWIGLU_BWD ? BM * BN * 4 : BM * BN * 2;
-  constexpr int LDS_CHUNKS = (SWAP && STG_BYTES > 2 * STAGE * 16) ? STG_BYTES / 16 : 2 * STAGE;
-  static_assert(LDS_CHUNKS * 16 <= 160 * 1024, "LDS budget of one workgroup");
-
-  __shared__ u32x4_t lds[LDS_CHUNKS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WAVES_N;
-  const int wn = wave % WAVES_N;
-
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  if (bid >= p.total) return;
-
-  int e, m0, n_tile, m_valid, kdim;
-  int64_t crow0;  // ragged M: first C row of the tile
-  const bf16_t *Ab;
-  const bf16_t *Bb;
-  if (!RAGGED_K) {
-    n_tile = bid % p.n_tiles;
-    const int mslot = bid / p.n_tiles;
-    int mt;
-    if (!find_m_tile<BM>(p.offsets, p.E, mslot, e, mt)) return;
-    const int row0 = p.offsets[e];
-    const int me = p.offsets[e + 1] - row0;
-    m0 = mt * BM;
-    m_valid = min(BM, me - m0);
-    crow0 = (int64_t)row0 + m0;
-    Ab = p.A + crow0 * p.lda;
-    Bb = p.B + (int64_t)e * p.strideB;
-    kdim = p.K;
-  } else {
-    const int per_e = p.m_tiles * p.n_tiles;
-    const int slot = bid / per_e;
-    e = p.order ? p.order[slot] : slot;
-    const int r = bid - slot * per_e;
-    const int mt = r / p.n_tiles;
-    n_tile = r - mt * p.n_tiles;
-    const int row0 = p.offsets[e];
-    kdim = p.offsets[e + 1] - row0;
-    if (kdim <= 0) return;  // empty expert: dW stays bit-identical
-    m0 = mt * BM;
-    m_valid = min(BM, p.M - m0);
-    crow0 = 0;
-    Ab = p.A + (int64_t)row0 * p.lda;
-    Bb = p.B + (int64_t)row0 * p.ldb;
-  }
-
-  // Global row of B-tile row r (k-contiguous B), -1 when past the end.
-  auto b_row = [&](int r) -> int {
-    if (EPI == EPI_SWIGLU_FWD) {
-      const int wcol = r / WN, q = r % WN;
-      const int g = n_tile * (BN / 2) + wcol * (WN / 2) + (q % (WN / 2));
-      return g < p.N ? (q < WN / 2 ? g : p.F + g) : -1;
-    } else {
-      const int n = n_tile * BN + r;
-      return n < p.N ? n : -1;
-    }
-  };
-
-  u32x4_t ra[A_NL > 0 ? A_NL : 1];
-  u32x4_t rb[B_NL > 0 ? B_NL : 1];
-  u32x4_t ta[A_TR > 0 ? A_TR : 1][8];
-  u32x4_t tb[B_TR > 0 ? B_TR : 1][8];
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-
-  auto load_tiles = [&](int k0) {
-    if (!AT) {
-#pragma unroll
-      for (int i = 0; i < A_NL; ++i) {
-        const int c = i * 256 + tid;
-        const int r = c >> 3, ch = c & 7;
-        const int rr = r < m_valid ? r : m_valid - 1;
-        ra[i] = ld16(Ab + (int64_t)rr * p.lda + k0 + ch * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_TR; ++i) {
-        const int sidx = i * 256 + tid;
-        const int xb = sidx % (BM / 8), kb = sidx / (BM / 8);
-        const bool on = sidx < A_SUB && xb * 8 < m_valid;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int kk = k0 + kb * 8 + q;
-          ta[i][q] = (on && kk < kdim) ? ld16(Ab + (int64_t)kk * p.lda + m0 + xb * 8) : zero4;
-        }
-      }
-    }
-    if (!BT) {
-#pragma unroll
-      for (int i = 0; i < B_NL; ++i) {
-        const int c = i * 256 + tid;
-        const int r = c >> 3, ch = c & 7;
-        const int g = b_row(r);
-        rb[i] = g >= 0 ? ld16(Bb + (int64_t)g * p.ldb + k0 + ch * 8) : zero4;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_TR; ++i) {
-        const int sidx = i * 256 + tid;
-        const int xb = sidx % (BN / 8), kb = sidx / (BN / 8);
-        const int n = n_tile * BN + xb * 8;
-        const bool on = sidx < B_SUB && n < p.N;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int kk = k0 + kb * 8 + q;
-          tb[i][q] = (on && kk < kdim) ? ld16(Bb + (int64_t)kk * p.ldb + n) : zero4;
-        }
-      }
-    }
-  };
-
-  auto store_tiles = [&](int buf) {
-    u32x4_t *As = lds + buf * STAGE;
-    u32x4_t *Bs = As + A_CHUNKS;
-    if (!AT) {
-#pragma unroll
-      for (int i = 0; i < A_NL; ++i) {
-        const int c = i * 256 + tid;
-        const int r = c >> 3, ch = c & 7;
-        As[r * 8 + (ch ^ swz(r))] = ra[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_TR; ++i) {
-        const int sidx = i * 256 + tid;
-        if (sidx < A_SUB) {
-          const int xb = sidx % (BM / 8), kb = sidx / (BM / 8);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            u32x4_t o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = pick_pair(ta[i][2 * q][j >> 1], ta[i][2 * q + 1][j >> 1], j & 1);
-            const int r = xb * 8 + j;
-            As[r * 8 + (kb ^ swz(r))] = o;
-          }
-        }
-      }
-    }
-    if (!BT) {
-#pragma unroll
-      for (int i = 0; i < B_NL; ++i) {
-        const int c = i * 256 + tid;
-        const int r = c >> 3, ch = c & 7;
-        Bs[r * 8 + (ch ^ swz(r))] = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_TR; ++i) {
-        const int sidx = i * 256 + tid;
-        if (sidx < B_SUB) {
-          const int xb = sidx % (BN / 8), kb = sidx / (BN / 8);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            u32x4_t o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = pick_pair(tb[i][2 * q][j >> 1], tb[i][2 * q + 1][j >> 1], j & 1);
-            const int r = xb * 8 + j;
-            Bs[r * 8 + (kb ^ swz(r))] = o;
-          }
-        }
-      }
-    }
-  };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int nk = (kdim + kBK - 1) / kBK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
-  const int l32 = lane & 31;
-  const int lhi = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * kBK);
-    const u32x4_t *As = lds + cur * STAGE;
-    const u32x4_t *Bs = As + A_CHUNKS;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ch = ks * 2 + lhi;
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM + i * 32 + l32;
-        af[i] = __builtin_bit_cast(bf16x8_t, As[r * 8 + (ch ^ swz(r))]);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WN + j * 32 + l32;
-        bfr[j] = __builtin_bit_cast(bf16x8_t, Bs[r * 8 + (ch ^ swz(r))]);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-    }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
-    __syncthreads();
-  }
-
-  epilogue<BM, BN, WM, WN, EPI>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
-}
-
-// ---------------------------------------------------------------------------
-// Forward products (both operands k-contiguous): LDS stages filled by the
-// gfx950 LDS DMA (global_load_lds_dwordx4), so that no tile data passes
-// through registers. Each stage is 64 deep in k, so every tile row of a stage
-// is one full 128-byte line and the L1 issues half as many L2 requests as
-// with 64-byte rows: the per-CU limit on outstanding requests, not the
-// matrix cores, bounds these products.
-// ---------------------------------------------------------------------------
-
-constexpr int kDmaBK = 64;  // k per stage
 constexpr int kGroupM = 4;  // row tiles per group in the ragged-M tile order
+// k per LDS stage and ring slots: 64-deep stages make every k-contiguous tile
+// row one 128-byte line; two slots of a 256x256 tile fill 128 KB of LDS (a
+// 4-slot ring of 32-deep stages measured 5-10% slower on every product).
+constexpr int kStageK = 64;
+constexpr int kStages = 2;
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 
@@ -564,20 +314,27 @@ MOE_DEVICE i16x4_t lds_read_tr16(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t *)(p));
 }
 
-// One operand's tile in an LDS stage, filled by DMA.
+// One operand's tile in an LDS stage of BK k values, filled by DMA.
 //  KM = false: the source is k-contiguous (rows = m or n). The tile is
-//    [ROWS][64] bf16 in 128-byte rows; chunk c of row r sits at c ^ swz(r).
+//    [ROWS][BK] bf16; chunk c of row r sits at c ^ kc_swz(r).
 //  KM = true:  the source is k-major (rows = k, contiguous along m or n).
 //    The tile is [64][ROWS] bf16; chunk c of row k sits at c ^ 4*(k % 4),
 //    which keeps the transposing fragment reads free of bank conflicts.
 // Every DMA instruction of a wave writes 1 KB of contiguous LDS.
-template <int ROWS, bool KM, int NW>
+// Chunk swizzle of a k-contiguous tile row with CPR 16-byte chunks (8 for
+// 128-byte rows, 4 for 64-byte rows), conflict-free for the fragment reads.
+template <int CPR>
+MOE_DEVICE int kc_swz(int r) {
+  return CPR == 8 ? swz(r) : ((r >> 2) & 3);
+}
+
+template <int ROWS, bool KM, int NW, int BK>
 struct Operand {
   static constexpr int NT = NW * 64;
-  static constexpr int BYTES = ROWS * kDmaBK * 2;
+  static constexpr int BYTES = ROWS * BK * 2;
   static constexpr int NDMA = BYTES / (NT * 16);
   static_assert(NDMA * NT * 16 == BYTES, "tile/thread mismatch");
-  static constexpr int ROWB = KM ? ROWS * 2 : 128;  // bytes per LDS tile row
+  static constexpr int ROWB = KM ? ROWS * 2 : BK * 2;  // bytes per LDS tile row
   static constexpr int CPR = ROWB / 16;             // 16-byte chunks per LDS row
   static constexpr int RPI = 1024 / ROWB;           // LDS rows per DMA instruction
   static_assert(!KM || CPR >= 16, "k-major tiles need at least 128 columns");
@@ -595,7 +352,7 @@ struct Operand {
       const int r = (i * NW + wave) * RPI + lane / CPR;
       const int phys = lane % CPR;
       if (!KM) {
-        const int c = phys ^ swz(r);
+        const int c = phys ^ kc_swz<CPR>(r);
         ptr[i] = base + (int64_t)row_map(r) * ld + c * 8;
         krow[i] = 0;
       } else {
@@ -628,7 +385,8 @@ struct Operand {
     if (!KM) {
       const int r = rb + (lane & 31);
       const int c = ks * 2 + (lane >> 5);
-      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(tile + (r * 8 + (c ^ swz(r))) * 16));
+      return __builtin_bit_cast(bf16x8_t,
+                                *reinterpret_cast<const u32x4_t *>(tile + (r * CPR + (c ^ kc_swz<CPR>(r))) * 16));
     } else {
       const int b = lane & 15, g = lane >> 4;
       const int col = rb + 16 * (g & 1) + 4 * (b & 3);
@@ -649,7 +407,7 @@ struct Operand {
 // stage in flight while the current one is consumed. A and B are each either
 // k-contiguous or k-major (transposed in the fragment reads). Ragged M
 // (forward, dgrad) or ragged K (wgrad) over experts.
-template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K>
+template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES>
 __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   constexpr int NT = NW * 64;
   constexpr int WAVES_N = BN / WN;
@@ -659,10 +417,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
   static_assert(RAGGED_K == (EPI == EPI_ACC_F32), "weight gradients are the ragged-K products");
   constexpr bool SWAP = EPI != EPI_ACC_F32;
-  using OpA = Operand<BM, AKM, NW>;
-  using OpB = Operand<BN, BKM, NW>;
+  using OpA = Operand<BM, AKM, NW, BK>;
+  using OpB = Operand<BN, BKM, NW, BK>;
   constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
-  constexpr int RING_BYTES = 2 * STAGE_BYTES;
+  constexpr int RING_BYTES = STAGES * STAGE_BYTES;
   constexpr int STG_BYTES = !SWAP ? 0 : BM * BN * 2;
   constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
@@ -736,8 +494,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int kt) {
-    const uint32_t sb = lds0 + (uint32_t)((kt & 1) * STAGE_BYTES);
-    const int k0 = kt * kDmaBK;
+    const uint32_t sb = lds0 + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+    const int k0 = kt * BK;
     opa.issue(k0, p.lda, kdim, sb, wave_u);
     opb.issue(k0, p.ldb, kdim, sb + OpA::BYTES, wave_u);
   };
@@ -750,19 +508,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = (kdim + kDmaBK - 1) / kDmaBK;
-  constexpr int KS = kDmaBK / 16;
+  const int nk = (kdim + BK - 1) / BK;
+  constexpr int KS = BK / 16;
   bf16x8_t af[2][FM], bfr[2][FN];
   // ragged K: the last stage's rows past kdim are zeroed in the A fragments
   auto load_frags = [&](int stage, int ks, int set, bool tail) {
-    const char *sa = reinterpret_cast<const char *>(lds) + (stage & 1) * STAGE_BYTES;
+    const char *sa = reinterpret_cast<const char *>(lds) + (stage % STAGES) * STAGE_BYTES;
     const char *sb = sa + OpA::BYTES;
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[set][i] = opa.frag(sa, wm * WM + i * 32, ks, lane);
 #pragma unroll
     for (int j = 0; j < FN; ++j) bfr[set][j] = opb.frag(sb, wn * WN + j * 32, ks, lane);
     if (RAGGED_K && tail) {
-      const int kbase = stage * kDmaBK + ks * 16 + 8 * (lane >> 5);
+      const int kbase = stage * BK + ks * 16 + 8 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -796,15 +554,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     if (NREAD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - PAIRS, 0);
   };
 
-  // Stage kt+1 is in flight while stage kt is consumed. The barrier of
-  // iteration kt sits before its last step: every wave has then read all of
-  // stage kt (waited with lgkmcnt) and stage kt+1 has landed, so stage kt+2
-  // can be issued into the slot of stage kt.
+  // A ring of STAGES slots: stages kt+1 .. kt+STAGES-1 are in flight while
+  // stage kt is consumed. The barrier of iteration kt sits before its last
+  // step: every wave has then read all of stage kt (waited with lgkmcnt) and
+  // stage kt+1 has landed, so stage kt+STAGES can be issued into the slot of
+  // stage kt.
   constexpr int PER_STAGE = OpA::NDMA + OpB::NDMA;
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 1) wait_vm<PER_STAGE>();
-  else wait_vm<0>();
+  // wait until at most `younger` whole stages are still in flight
+  auto wait_stages = [&](int younger) {
+    if (STAGES > 3 && younger >= 3) wait_vm<3 * PER_STAGE>();
+    else if (STAGES > 2 && younger == 2) wait_vm<2 * PER_STAGE>();
+    else if (younger == 1) wait_vm<PER_STAGE>();
+    else wait_vm<0>();
+  };
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st)
+    if (st < nk) issue(st);
+  wait_stages(min(nk, STAGES) - 1);
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, 0, nk == 1);
 
@@ -818,9 +584,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_lds();
-    wait_vm<0>();
+    // issued so far: stages up to min(kt+STAGES-1, nk-1); stage kt+1 needed
+    wait_stages(min(STAGES - 2, nk - 2 - kt));
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < nk) issue(kt + 2);
+    if (kt + STAGES < nk) issue(kt + STAGES);
     mfmas((KS - 1) & 1);
     // step 0 of stage kt+1 (on the last pass a harmless read of a stale slot,
     // kept unconditional so that it interleaves with the MFMAs above)
@@ -852,20 +619,13 @@ __global__ __launch_bounds__(256) void expert_order_kernel(const int32_t *__rest
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool AT, bool BT, int EPI, bool RAGGED_K>
-static hipError_t run_gemm(GemmParams p, hipStream_t s) {
-  if (p.total <= 0) return hipSuccess;
-  const int grid = (p.total + 7) / 8 * 8;
-  gg_bf16_kernel<BM, BN, WM, WN, AT, BT, EPI, RAGGED_K><<<dim3((unsigned)grid), 256, 0, s>>>(p);
-  return hipGetLastError();
-}
-
 template <int BM, int BN, int WM, int WN, bool AKM, bool BKM, int EPI, bool RAGGED_K>
 static hipError_t run_dma(GemmParams p, hipStream_t s) {
   if (p.total <= 0) return hipSuccess;
   constexpr int NW = (BM / WM) * (BN / WN);
   const int grid = RAGGED_K ? (p.total + 63) / 64 * 64 : (p.total + 7) / 8 * 8;
-  gg_dma_kernel<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K><<<dim3((unsigned)grid), NW * 64, 0, s>>>(p);
+  gg_dma_kernel<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, kStageK, kStages>
+      <<<dim3((unsigned)grid), NW * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
