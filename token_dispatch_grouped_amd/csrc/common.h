@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define MOE_DEVICE __device__ __forceinline__
 
 namespace moe {

@@ -16,9 +16,13 @@
 
 namespace moe {
 
+// The kernels are instantiated for a maximum slot count KMAX >= k and fully
+// unrolled over it, so that all k row indices (and weights) are loaded first
+// and all k row accesses of a thread are in flight together.
+
 // A4: x_perm[row_of_slot[t,j]] = x[t]. Each source chunk is read once and
 // written k times.
-template <typename T>
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void permute_kernel(const T *__restrict__ x, const int32_t *__restrict__ ros,
                                                       T *__restrict__ xp, int64_t ntok, int nc, int k) {
   const int64_t nrows = ntok * k;
@@ -28,16 +32,17 @@ __global__ __launch_bounds__(256) void permute_kernel(const T *__restrict__ x, c
   const int c = (int)(g - t * nc);
   if (t >= ntok) return;
   const int64_t ld = (int64_t)nc * V;
+  int64_t row[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) row[j] = j < k ? ros[t * k + j] : -1;
   const u32x4_t v = ld16(x + t * ld + (int64_t)c * V);
-  const int32_t *r = ros + t * k;
-  for (int j = 0; j < k; ++j) {
-    const int64_t row = r[j];
-    if ((uint64_t)row < (uint64_t)nrows) st16(xp + row * ld + (int64_t)c * V, v);
-  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k && (uint64_t)row[j] < (uint64_t)nrows) st16(xp + row[j] * ld + (int64_t)c * V, v);
 }
 
 // A7: out[t] = sum_j w[t,j] y[row_of_slot[t,j]].
-template <typename T>
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, const float *__restrict__ tw,
                                                       const int32_t *__restrict__ ros, T *__restrict__ out,
                                                       int64_t ntok, int nc, int k) {
@@ -47,17 +52,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
   const int c = (int)(g - t * nc);
   if (t >= ntok) return;
   const int64_t ld = (int64_t)nc * V;
+  const int64_t nrows = ntok * k;
+  int64_t row[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    row[j] = j < k ? ros[t * k + j] : -1;
+    w[j] = j < k ? tw[t * k + j] : 0.f;
+  }
+  u32x4_t raw[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
+    raw[j] = ok ? ld16(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
+  }
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float w = tw[t * k + j];
-    const int64_t row = ros[t * k + j];
-    if ((uint64_t)row >= (uint64_t)(ntok * k)) continue;
-    float v[V];
-    Elem<T>::unpack(ld16(y + row * ld + (int64_t)c * V), v);
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+  for (int j = 0; j < KMAX; ++j) {
+    float v[V];
+    Elem<T>::unpack(raw[j], v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
   }
   st16(out + t * ld + (int64_t)c * V, Elem<T>::pack(acc));
 }
@@ -65,7 +82,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
 // B1: dy[row] = w[t,j] dout[t];  dtopk_w[t,j] = <dout[t], y[row]>.
 // One wavefront per token: each lane holds CPL chunks of dout, the k dot
 // products are reduced across the wavefront.
-template <typename T, int CPL>
+template <typename T, int CPL, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ dout, const T *__restrict__ y,
                                                           const float *__restrict__ tw,
                                                           const int32_t *__restrict__ ros, T *__restrict__ dy,
@@ -75,43 +92,54 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ 
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= ntok) return;
   const int64_t ld = (int64_t)nc * V;
-  float g[CPL][V];
+  const int64_t nrows = ntok * k;
+  int64_t row[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    row[j] = j < k ? ros[t * k + j] : -1;
+    w[j] = j < k ? tw[t * k + j] : 0.f;
+  }
+  float dot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) dot[j] = 0.f;
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
     const int c = lane + q * 64;
-    if (c < nc) {
-      Elem<T>::unpack(ld16(dout + t * ld + (int64_t)c * V), g[q]);
-    } else {
+    if (c >= nc) break;
+    float gv[V];
+    Elem<T>::unpack(ld16(dout + t * ld + (int64_t)c * V), gv);
+    u32x4_t raw[KMAX];
 #pragma unroll
-      for (int i = 0; i < V; ++i) g[q][i] = 0.f;
+    for (int j = 0; j < KMAX; ++j) {
+      const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
+      raw[j] = ok ? ld16(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
     }
-  }
-  for (int j = 0; j < k; ++j) {
-    const float w = tw[t * k + j];
-    const int64_t row = ros[t * k + j];
-    const bool in = (uint64_t)row < (uint64_t)(ntok * k);
-    float dot = 0.f;
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const int c = lane + q * 64;
-      if (c < nc && in) {
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k && (uint64_t)row[j] < (uint64_t)nrows) {
         float v[V], o[V];
-        Elem<T>::unpack(ld16(y + row * ld + (int64_t)c * V), v);
+        Elem<T>::unpack(raw[j], v);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-          dot = fmaf(g[q][i], v[i], dot);
-          o[i] = w * g[q][i];
+          dot[j] = fmaf(gv[i], v[i], dot[j]);
+          o[i] = w[j] * gv[i];
         }
-        st16(dy + row * ld + (int64_t)c * V, Elem<T>::pack(o));
+        st16(dy + row[j] * ld + (int64_t)c * V, Elem<T>::pack(o));
       }
     }
-    dot = wave_sum(dot);
-    if (lane == 0) dtw[t * k + j] = dot;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const float d = wave_sum(dot[j]);
+      if (lane == 0) dtw[t * k + j] = d;
+    }
   }
 }
 
 // B7: dx[t] = sum_j dx_perm[row_of_slot[t,j]] (+ dx_extra[t]).
-template <typename T>
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(const T *__restrict__ dxp, const int32_t *__restrict__ ros,
                                                           const float *__restrict__ extra, T *__restrict__ dx,
                                                           int64_t ntok, int nc, int k) {
@@ -121,14 +149,23 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T *__restrict__ 
   const int c = (int)(g - t * nc);
   if (t >= ntok) return;
   const int64_t ld = (int64_t)nc * V;
+  const int64_t nrows = ntok * k;
+  int64_t row[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) row[j] = j < k ? ros[t * k + j] : -1;
+  u32x4_t raw[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
+    raw[j] = ok ? ld16(dxp + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
+  }
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t row = ros[t * k + j];
-    if ((uint64_t)row >= (uint64_t)(ntok * k)) continue;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
     float v[V];
-    Elem<T>::unpack(ld16(dxp + row * ld + (int64_t)c * V), v);
+    Elem<T>::unpack(raw[j], v);
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] += v[i];
   }
@@ -149,53 +186,72 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T *__restrict__ 
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(int64_t items) { return (unsigned)((items + 255) / 256); }
 
+// Calls f(std::integral_constant<int, KMAX>) with the smallest KMAX in
+// {1, 2, 4, 8, 16} that is >= k.
+template <typename F>
+static void with_kmax(int k, F &&f) {
+  if (k <= 1) f(std::integral_constant<int, 1>{});
+  else if (k <= 2) f(std::integral_constant<int, 2>{});
+  else if (k <= 4) f(std::integral_constant<int, 4>{});
+  else if (k <= 8) f(std::integral_constant<int, 8>{});
+  else f(std::integral_constant<int, 16>{});
+}
+
+template <typename T>
+static void permute_t(const void *x, const int32_t *ros, void *xp, int64_t T_, int d, int k, hipStream_t s) {
+  const int nc = d / Elem<T>::kVec;
+  with_kmax(k, [&](auto km) {
+    constexpr int KM = decltype(km)::value;
+    permute_kernel<T, KM><<<blocks_for(T_ * nc), 256, 0, s>>>((const T *)x, ros, (T *)xp, T_, nc, k);
+  });
+}
+
 hipError_t launch_permute(const void *x, const int32_t *row_of_slot, void *x_perm, int64_t T, int d, int k,
                           bool bf16, hipStream_t s) {
   LaunchScope scope("permute", s);
-  if (bf16) {
-    const int nc = d / 8;
-    permute_kernel<bf16_t><<<blocks_for(T * nc), 256, 0, s>>>((const bf16_t *)x, row_of_slot, (bf16_t *)x_perm, T,
-                                                              nc, k);
-  } else {
-    const int nc = d / 4;
-    permute_kernel<float><<<blocks_for(T * nc), 256, 0, s>>>((const float *)x, row_of_slot, (float *)x_perm, T, nc,
-                                                             k);
-  }
+  if (bf16) permute_t<bf16_t>(x, row_of_slot, x_perm, T, d, k, s);
+  else permute_t<float>(x, row_of_slot, x_perm, T, d, k, s);
   return hipGetLastError();
+}
+
+template <typename T>
+static void combine_t(const void *y, const float *tw, const int32_t *ros, void *out, int64_t T_, int d, int k,
+                      hipStream_t s) {
+  const int nc = d / Elem<T>::kVec;
+  with_kmax(k, [&](auto km) {
+    constexpr int KM = decltype(km)::value;
+    combine_kernel<T, KM><<<blocks_for(T_ * nc), 256, 0, s>>>((const T *)y, tw, ros, (T *)out, T_, nc, k);
+  });
 }
 
 hipError_t launch_combine(const void *y, const float *topk_w, const int32_t *row_of_slot, void *out, int64_t T,
                           int d, int k, bool bf16, hipStream_t s) {
   LaunchScope scope("combine", s);
-  if (bf16) {
-    const int nc = d / 8;
-    combine_kernel<bf16_t><<<blocks_for(T * nc), 256, 0, s>>>((const bf16_t *)y, topk_w, row_of_slot,
-                                                              (bf16_t *)out, T, nc, k);
-  } else {
-    const int nc = d / 4;
-    combine_kernel<float><<<blocks_for(T * nc), 256, 0, s>>>((const float *)y, topk_w, row_of_slot, (float *)out,
-                                                             T, nc, k);
-  }
+  if (bf16) combine_t<bf16_t>(y, topk_w, row_of_slot, out, T, d, k, s);
+  else combine_t<float>(y, topk_w, row_of_slot, out, T, d, k, s);
   return hipGetLastError();
+}
+
+template <typename T, int CPL>
+static void combine_bwd_c(const T *dout, const T *y, const float *tw, const int32_t *ros, T *dy, float *dtw,
+                          int64_t ntok, int nc, int k, hipStream_t s) {
+  const unsigned grid = (unsigned)((ntok + 3) / 4);
+  with_kmax(k, [&](auto km) {
+    constexpr int KM = decltype(km)::value;
+    combine_bwd_kernel<T, CPL, KM><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
+  });
 }
 
 template <typename T>
 static void combine_bwd_dispatch(const T *dout, const T *y, const float *tw, const int32_t *ros, T *dy,
                                  float *dtw, int64_t ntok, int nc, int k, hipStream_t s) {
-  const unsigned grid = (unsigned)((ntok + 3) / 4);
   const int cpl = (nc + 63) / 64;
-  if (cpl <= 1)
-    combine_bwd_kernel<T, 1><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
-  else if (cpl <= 2)
-    combine_bwd_kernel<T, 2><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
-  else if (cpl <= 4)
-    combine_bwd_kernel<T, 4><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
-  else if (cpl <= 8)
-    combine_bwd_kernel<T, 8><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
-  else if (cpl <= 16)
-    combine_bwd_kernel<T, 16><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
-  else
-    combine_bwd_kernel<T, 32><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
+  if (cpl <= 1) combine_bwd_c<T, 1>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
+  else if (cpl <= 2) combine_bwd_c<T, 2>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
+  else if (cpl <= 4) combine_bwd_c<T, 4>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
+  else if (cpl <= 8) combine_bwd_c<T, 8>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
+  else if (cpl <= 16) combine_bwd_c<T, 16>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
+  else combine_bwd_c<T, 32>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
 }
 
 hipError_t launch_combine_bwd(const void *dout, const void *y, const float *topk_w, const int32_t *row_of_slot,
@@ -210,18 +266,21 @@ hipError_t launch_combine_bwd(const void *dout, const void *y, const float *topk
   return hipGetLastError();
 }
 
+template <typename T>
+static void permute_bwd_t(const void *dxp, const int32_t *ros, const float *extra, void *dx, int64_t T_, int d,
+                          int k, hipStream_t s) {
+  const int nc = d / Elem<T>::kVec;
+  with_kmax(k, [&](auto km) {
+    constexpr int KM = decltype(km)::value;
+    permute_bwd_kernel<T, KM><<<blocks_for(T_ * nc), 256, 0, s>>>((const T *)dxp, ros, extra, (T *)dx, T_, nc, k);
+  });
+}
+
 hipError_t launch_permute_bwd(const void *dx_perm, const int32_t *row_of_slot, const float *dx_extra, void *dx,
                               int64_t T, int d, int k, bool bf16, hipStream_t s) {
   LaunchScope scope("permute_bwd", s);
-  if (bf16) {
-    const int nc = d / 8;
-    permute_bwd_kernel<bf16_t><<<blocks_for(T * nc), 256, 0, s>>>((const bf16_t *)dx_perm, row_of_slot, dx_extra,
-                                                                  (bf16_t *)dx, T, nc, k);
-  } else {
-    const int nc = d / 4;
-    permute_bwd_kernel<float><<<blocks_for(T * nc), 256, 0, s>>>((const float *)dx_perm, row_of_slot, dx_extra,
-                                                                 (float *)dx, T, nc, k);
-  }
+  if (bf16) permute_bwd_t<bf16_t>(dx_perm, row_of_slot, dx_extra, dx, T, d, k, s);
+  else permute_bwd_t<float>(dx_perm, row_of_slot, dx_extra, dx, T, d, k, s);
   return hipGetLastError();
 }
 
