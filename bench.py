@@ -44,15 +44,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "e5e3357abf8bbe3ac0d2103211c6f13662e285c37754b762515e3cba7cec3fac",
+    "sources_sha256": "d88eef1400cf41d39804cdf33603b4402b5d77eb6e36a3e399eb736a23b6406d",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (10.441 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.216 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (5.756 + 1.375) * 2 ** 30,
-        "gg_gateup_dgrad": (4.484 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (11.537 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (5.738 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.188 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.162 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (6.025 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.373 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (11.506 + 0.645) * 2 ** 30,
     },
 }
 
