@@ -12,6 +12,13 @@ runs) over the stream time of the timed steps. ``roofline`` describes the
 dominant kernel, timed with HIP events on the launch stream inside the timed
 region; ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the
 same workload on this host's cores.
+
+``--mode recompute`` runs the same step with MOE_FLAG_RECOMPUTE (no h/a kept
+between forward and backward; the backward recomputes them): ``value`` stays
+the algorithmic rate (the recompute product is extra work the method does not
+need) and ``executed_tflops`` counts it. ``--mode nograd`` times the forward
+alone under MOE_FLAG_RECOMPUTE (no activations kept), value = 6*R*d*F per
+step over its time. The default (``train``) is the headline measurement.
 """
 from __future__ import annotations
 
@@ -26,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd TFLOP/s & % bf16 MFMA peak; permute/combine GB/s"
+METRIC_NOGRAD = "MoE layer forward (no-grad) TFLOP/s & % bf16 MFMA peak; permute/combine GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
@@ -33,7 +41,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 GEMM_KERNELS = {
     # name: FLOPs per launch in units of R*d*F
     "gg_gateup_fwd": 4, "gg_down_fwd": 2, "gg_down_dgrad": 2, "gg_down_wgrad": 2, "gg_gateup_dgrad": 4,
-    "gg_gateup_wgrad": 4,
+    "gg_gateup_wgrad": 4, "gg_gateup_recompute": 4,
 }
 MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 
@@ -95,15 +103,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle's timed sample (0 disables the CPU baseline)")
     ap.add_argument("--renorm", action="store_true")
+    ap.add_argument("--mode", choices=("train", "recompute", "nograd"), default="train",
+                    help="train: forward+backward keeping h and a (default); recompute: forward+backward with "
+                         "MOE_FLAG_RECOMPUTE; nograd: forward alone with MOE_FLAG_RECOMPUTE")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes before timing (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(w, inp, target_s):
+def cpu_baseline(w, inp, target_s, fwd_only=False):
     """Time the fp64 oracle (as it is) on the first T_s tokens of the first
-    microbatch: one forward+backward, T_s sized to take about target_s."""
+    microbatch: one forward+backward (forward alone if fwd_only), T_s sized
+    to take about target_s."""
     import numpy as np
     import oracle
     from workloads import to_f64
@@ -128,7 +140,8 @@ def cpu_baseline(w, inp, target_s):
             _, sv = oracle.layer_fwd(x, wgu, wdn, w.k, w_router=wr, bias=bias)
         else:
             _, sv = oracle.layer_fwd(x, wgu, wdn, w.k, logits=mb["logits"][:Ts].astype(np.float64))
-        oracle.layer_bwd(dout, sv, wgu, wdn, x=x, w_router=wr)
+        if not fwd_only:
+            oracle.layer_bwd(dout, sv, wgu, wdn, x=x, w_router=wr)
         return time.perf_counter() - t0
 
     # size the sample from a 1024-token probe (small probes overstate the
@@ -138,9 +151,10 @@ def cpu_baseline(w, inp, target_s):
     if dt < target_s and Ts < T_full:
         Ts = int(min(T_full, max(Ts, Ts * target_s / max(dt, 1e-3))))
         dt = run(Ts)
-    flops = w.flops_fwd_bwd(Ts)
+    flops = w.flops_fwd(Ts) if fwd_only else w.flops_fwd_bwd(Ts)
+    what = "forward" if fwd_only else "forward+backward"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, one forward+backward of the first {Ts} of {T_full} tokens "
+            "sample": f"fp64 NumPy oracle, one {what} of the first {Ts} of {T_full} tokens "
                       f"of the same inputs ({dt:.1f} s)"}
 
 
@@ -176,7 +190,8 @@ def main():
     dt = moe.MOE_DTYPE_BF16 if w.dtype == BF16 else moe.MOE_DTYPE_F32
     router = w.routing == "router"
     Tmax = max(max(w.microbatches), 1)
-    layer = MoeLayer(Tmax, w.d, w.E, w.k, w.F, dt, renorm=args.renorm, router=router)
+    layer = MoeLayer(Tmax, w.d, w.E, w.k, w.F, dt, renorm=args.renorm, router=router,
+                     recompute=args.mode != "train")
     W = inp["weights"]
     wgu, wdn = dev_t(W["w_gu"], w.dtype), dev_t(W["w_down"], w.dtype)
     wr = dev_t(W["w_router"], w.dtype) if router else None
@@ -191,11 +206,14 @@ def main():
     dw_r = torch.zeros(w.E, w.d, dtype=torch.float32, device=dev) if router else None
     torch.cuda.synchronize()
 
+    nograd = args.mode == "nograd"
+
     def step():
         for mb in mbs:
             T = mb["T"]
             layer.forward(T, mb["x"], wgu, wdn, logits=mb["logits"], w_router=wr, bias=bias)
-            layer.backward(T, mb["dout"], wgu, wdn, dw_gu, dw_dn, x=mb["x"], w_router=wr, dw_router=dw_r)
+            if not nograd:
+                layer.backward(T, mb["dout"], wgu, wdn, dw_gu, dw_dn, x=mb["x"], w_router=wr, dw_router=dw_r)
 
     if args.calibrate_copy > 0:
         src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device=dev).fill_(1)
@@ -226,7 +244,7 @@ def main():
     stream_ms = ev0.elapsed_time(ev1)
     ms_per_step = stream_ms / args.steps
 
-    flops_step = w.flops_fwd_bwd()
+    flops_step = w.flops_fwd() if nograd else w.flops_fwd_bwd()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     s = 2 if w.dtype == BF16 else 4
     peak = PEAK_BF16_TFLOPS if w.dtype == BF16 else PEAK_F32_TFLOPS
@@ -248,10 +266,14 @@ def main():
             entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
         kernels[name] = entry
 
-    gemm_ms = sum(kernels[n]["total_ms_per_step"] for n in kernels if n.replace("_f32", "") in GEMM_KERNELS)
-    mem_ms = sum(kernels[n]["total_ms_per_step"] for n in kernels if n in MEM_KERNELS)
-    mem_by = sum(mem_bytes(n, mb["T"], w.d, w.k, s, router) for n in MEM_KERNELS for mb in mbs)
-    gemm_tf = (18.0 * sum(mb["T"] for mb in mbs) * w.k * w.d * w.F) / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
+    gemm_names = [n for n in kernels if n.replace("_f32", "") in GEMM_KERNELS]
+    gemm_ms = sum(kernels[n]["total_ms_per_step"] for n in gemm_names)
+    gemm_fl = sum(GEMM_KERNELS[n.replace("_f32", "")] * mb["T"] * w.k * w.d * w.F for n in gemm_names for mb in mbs)
+    mem_names = [n for n in kernels if n in MEM_KERNELS]
+    mem_ms = sum(kernels[n]["total_ms_per_step"] for n in mem_names)
+    mem_by = sum(mem_bytes(n, mb["T"], w.d, w.k, s, router) for n in mem_names for mb in mbs)
+    # executed GEMM FLOPs (the recompute product included) over GEMM time
+    gemm_tf = gemm_fl / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
     pc_gbps = mem_by / (mem_ms * 1e-3) / 1e9 if mem_ms else 0.0
 
     # dominant kernel: largest share of the step
@@ -271,10 +293,14 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None}
 
+    # the recompute product is work done beyond the method's own FLOPs
+    executed_fl = flops_step + (GEMM_KERNELS["gg_gateup_recompute"] * sum(mb["T"] for mb in mbs) * w.k * w.d * w.F
+                                if args.mode == "recompute" else 0.0)
     cfg = {"workload": w.name, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d, "E_local": w.E,
-           "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "description": w.description}
+           "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "mode": args.mode,
+           "description": w.description}
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_NOGRAD if nograd else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.dtype == BF16 else "f32", "data": "synthetic",
         "config": cfg,
@@ -283,13 +309,14 @@ def main():
         "grouped_gemm_pct_peak": round(100 * gemm_tf / peak, 2),
         "permute_combine_GBps": round(pc_gbps, 1),
         "permute_combine_pct_hbm": round(100 * pc_gbps / PEAK_HBM_GBPS, 2),
+        "executed_tflops": round(executed_fl / (ms_per_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 2),
         "kernels": kernels,
         "roofline": roof,
     }
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, fwd_only=nograd)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

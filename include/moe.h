@@ -68,9 +68,21 @@ typedef enum moe_status {
 
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
 
-/* Renormalise the k selected weights so that they sum to one. Without it the
- * weights are the full-softmax probabilities of the selected experts. */
-enum { MOE_FLAG_RENORM = 1u };
+/* MOE_FLAG_RENORM: renormalise the k selected weights so that they sum to
+ * one. Without it the weights are the full-softmax probabilities of the
+ * selected experts.
+ *
+ * MOE_FLAG_RECOMPUTE: keep no FFN activations between forward and backward
+ * (activation checkpointing of the expert FFN: Add MoE expert parallel
+ * training runtime, Summary; no-grad execution: Support pipeline parallelism
+ * in TrainerRank without exposing stage scheduling to callers, Acceptance).
+ * moe_grouped_gemm_fwd then takes h = a = NULL, never writes h and keeps a
+ * only in its workspace; it is also the forward to use when no backward
+ * follows. moe_grouped_gemm_bwd takes h = a = NULL and first recomputes h and
+ * a from x_perm into its workspace (one more gate/up product, bit-identical
+ * to the forward's), then writes dH over the recomputed h. Results equal
+ * those without the flag bit for bit. */
+enum { MOE_FLAG_RENORM = 1u, MOE_FLAG_RECOMPUTE = 2u };
 
 typedef struct moe_shape {
   int64_t T;      /* tokens in this microbatch (>= 0) */
@@ -145,7 +157,9 @@ moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *row
  * silu(z) = z / (1 + exp(-z)). The gate/up products feed the SwiGLU in fp32
  * before h and a are rounded. An expert with no rows costs nothing: tiles
  * are laid out on the device from `offsets`, which the host never reads.
- * ws: at least gemm_fwd_ws bytes (may be NULL when that size is 0).
+ * With MOE_FLAG_RECOMPUTE, h and a must be NULL: h is not written and a
+ * lives in ws. ws: at least gemm_fwd_ws bytes (may be NULL when that size
+ * is 0; it is R*F*s bytes with MOE_FLAG_RECOMPUTE).
  */
 moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, const void *w_gu,
                                 const void *w_down, const int32_t *offsets, void *h, void *a,
@@ -204,7 +218,9 @@ moe_status moe_route_bwd(const moe_shape *shape, const float *dtopk_w, const flo
  * caller zeroes them once. An expert with no rows leaves its dw slices
  * bit-identical. Each dw element is reduced by one workgroup in a fixed
  * order, so results are identical run to run.
- * ws: at least gemm_bwd_ws bytes.
+ * With MOE_FLAG_RECOMPUTE, h and a must be NULL; h and a are recomputed from
+ * x_perm into ws before the steps above, and dH overwrites the recomputed h.
+ * ws: at least gemm_bwd_ws bytes; dH occupies its first R*2F*s bytes.
  */
 moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const void *x_perm,
                                 const void *h, const void *a, const void *w_gu, const void *w_down,

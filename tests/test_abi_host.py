@@ -60,7 +60,7 @@ def shape(T=64, d=64, E=4, k=2, F=128, dtype=L.MOE_DTYPE_BF16, flags=0):
     (dict(E=257, k=2), L.MOE_ERR_UNSUPPORTED),
     (dict(E=32, k=17), L.MOE_ERR_UNSUPPORTED),
     (dict(dtype=7), L.MOE_ERR_UNSUPPORTED),
-    (dict(flags=2), L.MOE_ERR_UNSUPPORTED),
+    (dict(flags=4), L.MOE_ERR_UNSUPPORTED),              # unknown flag bit
     (dict(T=2 ** 28, E=8, k=8), L.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
 ])
 def test_shape_validation(kw, status):
@@ -129,6 +129,42 @@ def test_workspace_rules():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_grouped_gemm_bwd(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, stream=0)
     assert ei.value.status == L.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("dtype", [L.MOE_DTYPE_BF16, L.MOE_DTYPE_F32])
+def test_recompute_workspace_and_argument_rules(dtype):
+    """MOE_FLAG_RECOMPUTE: the forward workspace holds a [R,F]; the backward
+    workspace holds dH (over the recomputed h), the expert order and the
+    recomputed a; h and a must be NULL in both calls."""
+    T, d, E, k, F = 4096, 1024, 8, 2, 2816
+    es = 2 if dtype == L.MOE_DTYPE_BF16 else 4
+    R = T * k
+    plain = moe.moe_workspace_size(shape(T, d, E, k, F, dtype))
+    rc = moe.moe_workspace_size(shape(T, d, E, k, F, dtype, flags=L.MOE_FLAG_RECOMPUTE))
+    align = lambda n: (n + 255) // 256 * 256
+    assert plain[1] == 0 and rc[1] == align(R * F * es)
+    assert rc[0] == plain[0]
+    assert rc[2] == plain[2] + align(R * F * es)
+    s = shape(T, d, E, k, F, dtype, flags=L.MOE_FLAG_RECOMPUTE)
+    with pytest.raises(moe.MoeError) as ei:   # h given under recompute
+        moe.moe_grouped_gemm_fwd(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, rc[1], stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "h" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:   # forward workspace missing
+        moe.moe_grouped_gemm_fwd(s, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, stream=0)
+    assert ei.value.status == L.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:   # a given under recompute
+        moe.moe_grouped_gemm_bwd(s, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, rc[2],
+                                 stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "a" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:   # backward workspace one byte short
+        moe.moe_grouped_gemm_bwd(s, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, rc[2] - 1,
+                                 stream=0)
+    assert ei.value.status == L.MOE_ERR_WORKSPACE
+    # without the flag, h and a are required
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_grouped_gemm_fwd(shape(T, d, E, k, F, dtype), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, 0,
+                                 stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.parametrize("dtype", [L.MOE_DTYPE_BF16, L.MOE_DTYPE_F32])

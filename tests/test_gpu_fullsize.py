@@ -21,14 +21,14 @@ from workloads import BF16, F32, WORKLOADS, make_inputs, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _run_full(w, inp):
+def _run_full(w, inp, recompute=False):
     import torch
     import token_dispatch_grouped_amd as moe
     from token_dispatch_grouped_amd.layer import MoeLayer
     mb = inp["micro"][0]
     W = inp["weights"]
     T = mb["x"].shape[0]
-    layer = MoeLayer(T, w.d, w.E, w.k, w.F, moe.MOE_DTYPE_BF16)
+    layer = MoeLayer(T, w.d, w.E, w.k, w.F, moe.MOE_DTYPE_BF16, recompute=recompute)
     x = to_device(mb["x"], BF16)
     dout = to_device(mb["dout"], BF16)
     wgu = to_device(W["w_gu"], BF16)
@@ -190,3 +190,31 @@ def test_fullsize_microbatch_accumulation():
     for ee in range(w.E):
         if all(int(r["counts"][ee]) == 0 for r in routes):
             assert float(dw_gu[ee].abs().max()) == 0.0 and float(dw_dn[ee].abs().max()) == 0.0
+
+
+def test_fullsize_recompute_bitwise():
+    """At the 32k EP-share size, the recomputing backward gives the same
+    bits as the saved-activation path in every output and gradient (the
+    latter is checked against the oracle above)."""
+    import torch
+    w = WORKLOADS["ep_share_32k"]
+    print(f"[fullsize] recompute {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
+    inp = make_inputs(w)
+    lay_s, sv_s, g_s, dgu_s, ddn_s = _run_full(w, inp)
+    res_s = {"out": sv_s.out.clone(), "y": sv_s.y.clone(), "dh": g_s["dh"].clone(),
+             **{k: g_s[k].clone() for k in ("dy", "dtopk_w", "dlogits", "dx_perm", "dx")}}
+    a_saved = sv_s.a.clone()
+    del lay_s, sv_s, g_s
+    torch.cuda.empty_cache()
+    lay_r, sv_r, g_r, dgu_r, ddn_r = _run_full(w, inp, recompute=True)
+    assert lay_r.h is None and lay_r.a is None
+    for k, v in res_s.items():
+        got = sv_r.out if k == "out" else sv_r.y if k == "y" else g_r[k]
+        assert torch.equal(got, v), k
+    assert torch.equal(dgu_r, dgu_s) and torch.equal(ddn_r, ddn_s)
+    # the recomputed a sits after dH and the expert order in the backward workspace
+    R, F = w.T * w.k, w.F
+    align = lambda n: (n + 255) // 256 * 256
+    off = align(R * 2 * F * 2) + align(w.E * 4)
+    a_rc = lay_r.bwd_ws[off:off + R * F * 2].view(torch.bfloat16).view(R, F)
+    assert torch.equal(a_rc, a_saved)

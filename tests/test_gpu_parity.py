@@ -25,14 +25,16 @@ def _moe():
     return m, MoeLayer
 
 
-def gpu_run(w, inp, renorm=False, logits_override=None, sentinel=False):
-    """Run every microbatch forward+backward on the GPU; dW accumulate."""
+def gpu_run(w, inp, renorm=False, logits_override=None, sentinel=False, recompute=False):
+    """Run every microbatch forward+backward on the GPU; dW accumulate.
+    With recompute, h is not kept (None in the results) and a is read from
+    the forward workspace right after the forward."""
     import torch
     m, MoeLayer = _moe()
     dt = m.MOE_DTYPE_BF16 if w.dtype == BF16 else m.MOE_DTYPE_F32
     router = w.routing == "router"
     Tmax = max(max(w.microbatches), 1)
-    layer = MoeLayer(Tmax, w.d, w.E, w.k, w.F, dt, renorm=renorm, router=router)
+    layer = MoeLayer(Tmax, w.d, w.E, w.k, w.F, dt, renorm=renorm, router=router, recompute=recompute)
     if sentinel:
         for name in ("x_perm", "h", "a", "y", "out", "dy", "dx_perm", "dx", "logits", "topk_w", "dtopk_w",
                      "dlogits"):
@@ -58,9 +60,12 @@ def gpu_run(w, inp, renorm=False, logits_override=None, sentinel=False):
             lg = to_device(np.ascontiguousarray(lg, dtype=np.float32), F32)
         before = (dw_gu.clone(), dw_down.clone())
         sv = layer.forward(T, x, wgu, wdn, logits=lg, w_router=wr, bias=bias)
+        a_fwd = to_host64(layer.fwd_a_view(T)) if recompute else None
         g = layer.backward(T, dout, wgu, wdn, dw_gu, dw_down, x=x, w_router=wr, dw_router=dw_router)
         torch.cuda.synchronize()
-        r = {k: to_host64(getattr(sv, k)) for k in ("logits", "topk_w", "x_perm", "h", "a", "y", "out")}
+        r = {k: to_host64(getattr(sv, k)) for k in ("logits", "topk_w", "x_perm", "y", "out")}
+        r["h"] = None if recompute else to_host64(sv.h)
+        r["a"] = a_fwd if recompute else to_host64(sv.a)
         for k in ("topk_idx", "row_of_slot", "src_of_row", "counts", "offsets"):
             r[k] = getattr(sv, k).cpu().numpy()
         for k in ("dy", "dtopk_w", "dlogits", "dx_perm", "dx", "dh"):
@@ -128,6 +133,8 @@ def compare(w, gres, gacc, ores, oacc, renorm=False):
         errs["topk_w"] = assert_close("topk_w", g["topk_w"], o["topk_w"], TOL_ROUTING if w.routing != "router"
                                       else tol)
         for k in ("h", "a", "y", "out", "dy", "dtopk_w", "dlogits", "dx_perm", "dh", "dx"):
+            if g[k] is None:  # h is not kept under recompute
+                continue
             errs[k] = assert_close(f"mb{i} {k}", g[k], o[k], tol)
         if w.routing == "router":
             errs["dx_router"] = assert_close(f"mb{i} dx_router", g["dx_router"], o["dx_router"], tol)
@@ -276,3 +283,71 @@ def test_workspace_reuse_across_sizes():
     gres, gacc = gpu_run(w, inp)
     ores, oacc = oracle_run(w, inp)
     compare(w, gres, gacc, ores, oacc)
+
+
+# --- activation recompute (MOE_FLAG_RECOMPUTE) and no-grad forward ---------
+
+RECOMPUTE_CASES = [c for c in SMALL_CASES if c[0] in (
+    "tiny_f32_router", "bf16_ragged_tiles_zipf", "bf16_renorm_k8", "f32_zipf", "bf16_E256_k16", "bf16_single_expert")]
+
+
+def _assert_bitwise(a_res, a_acc, b_res, b_acc):
+    for i, (ra, rb) in enumerate(zip(a_res, b_res)):
+        for k in ra:
+            if ra[k] is None or rb[k] is None:
+                continue
+            assert np.array_equal(ra[k], rb[k], equal_nan=True), f"mb{i} {k} differs from the saved-activation run"
+    for k in a_acc:
+        assert np.array_equal(a_acc[k], b_acc[k]), f"{k} differs from the saved-activation run"
+
+
+@pytest.mark.parametrize("name,w,renorm", RECOMPUTE_CASES, ids=[c[0] for c in RECOMPUTE_CASES])
+def test_recompute_small(name, w, renorm):
+    """The recomputing backward matches the oracle to the bar and the
+    saved-activation path bit for bit (same kernels, same order)."""
+    print(f"[recompute] {name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F} {w.dtype}", flush=True)
+    inp = make_inputs(w)
+    gres, gacc = gpu_run(w, inp, renorm, recompute=True)
+    ores, oacc = oracle_run(w, inp, renorm)
+    compare(w, gres, gacc, ores, oacc, renorm)
+    sres, sacc = gpu_run(w, inp, renorm)
+    _assert_bitwise(gres, gacc, sres, sacc)
+
+
+def test_recompute_microbatch_accumulation():
+    """Microbatches T = 300, 77, 0, 513 on one recomputing layer: dW
+    accumulate, the empty microbatch leaves them bit-identical."""
+    w = small_workload(513, 128, 16, 4, 128, BF16, "zipf", seed=34, n_empty=2, micro_T=(300, 77, 0, 513))
+    inp = make_inputs(w)
+    gres, gacc = gpu_run(w, inp, recompute=True)
+    ores, oacc = oracle_run(w, inp)
+    compare(w, gres, gacc, ores, oacc)
+    assert gres[2]["dw_unchanged"]
+    sres, sacc = gpu_run(w, inp)
+    _assert_bitwise(gres, gacc, sres, sacc)
+
+
+def test_nograd_forward():
+    """Forward alone (no backward) under recompute, twice in a row on a
+    smaller then larger microbatch: out matches the oracle and the
+    saved-activation forward bit for bit; the layer owns no h or a."""
+    import torch
+    m, MoeLayer = _moe()
+    w = small_workload(700, 256, 8, 2, 192, BF16, "zipf", seed=38, n_empty=1, micro_T=(300, 700))
+    inp = make_inputs(w)
+    W = inp["weights"]
+    wgu, wdn = to_device(W["w_gu"], BF16), to_device(W["w_down"], BF16)
+    lay_rc = MoeLayer(700, w.d, w.E, w.k, w.F, m.MOE_DTYPE_BF16, recompute=True)
+    lay_sv = MoeLayer(700, w.d, w.E, w.k, w.F, m.MOE_DTYPE_BF16)
+    assert lay_rc.h is None and lay_rc.a is None
+    for mb in inp["micro"]:
+        T = mb["x"].shape[0]
+        x, lg = to_device(mb["x"], BF16), to_device(mb["logits"], F32)
+        o_rc = lay_rc.forward(T, x, wgu, wdn, logits=lg).out.clone()
+        o_sv = lay_sv.forward(T, x, wgu, wdn, logits=lg).out.clone()
+        torch.cuda.synchronize()
+        assert torch.equal(o_rc, o_sv)
+        assert torch.equal(lay_rc.fwd_a_view(T), lay_sv.a[:T * w.k])
+        out, _ = oracle.layer_fwd(to_f64(mb["x"], BF16), to_f64(W["w_gu"], BF16), to_f64(W["w_down"], BF16), w.k,
+                                  logits=mb["logits"].astype(np.float64))
+        assert_close("out (no-grad)", to_host64(o_rc), out, TOL[BF16])

@@ -4,7 +4,7 @@ The compute lives in ``libmoe_mi355x.so`` (HIP kernels for gfx950 behind the
 C ABI declared in ``include/moe.h``); this package is its Python binding.
 """
 from ._lib import (  # noqa: F401
-    MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_FLAG_RENORM, MOE_OK, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT,
+    MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_FLAG_RECOMPUTE, MOE_FLAG_RENORM, MOE_OK, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT,
     MOE_ERR_MISALIGNED, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MoeError, load, make_shape, moe_shape,
     moe_workspace_size, moe_route, moe_permute, moe_grouped_gemm_fwd, moe_unpermute_combine,
     moe_unpermute_combine_bwd, moe_route_bwd, moe_grouped_gemm_bwd, moe_permute_bwd, moe_status_string,

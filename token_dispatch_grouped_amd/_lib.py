@@ -25,6 +25,7 @@ MOE_ERR_HIP = 5
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_FLAG_RENORM = 1
+MOE_FLAG_RECOMPUTE = 2
 
 
 class MoeError(RuntimeError):

@@ -188,11 +188,13 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
           stg_put4(r, BN / 2 + col, BN, ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
         }
     __syncthreads();
-    flush(BN, (bf16_t *)p.C, p.ldc, [&](int c) {
-      if (c < BN / 2) return g0 + c < p.N ? g0 + c : -1;
-      const int g = g0 + c - BN / 2;
-      return g < p.N ? p.F + g : -1;
-    });
+    if (p.C) {  // NULL when h is not kept (the activations are recomputed later)
+      flush(BN, (bf16_t *)p.C, p.ldc, [&](int c) {
+        if (c < BN / 2) return g0 + c < p.N ? g0 + c : -1;
+        const int g = g0 + c - BN / 2;
+        return g < p.N ? p.F + g : -1;
+      });
+    }
     __syncthreads();
     // staged a = silu(gate) * up tile, BN/2 columns
 #pragma unroll
@@ -218,7 +220,9 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
     // DMA layout: wave instruction q fills 1 KB = 1024/(2*BN) staged rows;
     // lane l takes physical chunk l % (BN/8) of its row, i.e. logical chunk
     // phys ^ (row & 15). Rows past m_valid and columns past N are clamped
-    // (their results are never stored).
+    // (their results are never stored). Every h element a workgroup reads
+    // lies in its own output tile and is read before the band holding it is
+    // stored, so dH may overwrite h in place (p.C == p.H).
     static_assert(2 * WM * BN * 2 <= 160 * 1024, "two staged bands must fit in LDS");
     const int n0 = n_tile * BN;
     constexpr int CPR = BN / 8;
@@ -231,6 +235,7 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
     bf16_t *su_tile = stg + WM * BN;       // [WM][BN] h_up   -> dH_up
     for (int band = 0; band < WAVES_M; ++band) {
       const int rbase = band * WM;
+      if (rbase >= m_valid) break;  // uniform: the rest of the tile is past the expert's rows
 #pragma unroll
       for (int q = 0; q < NI; ++q) {
         const int r = (q * (NT / 64) + wv) * RPI + lane / CPR;
@@ -644,26 +649,32 @@ static int ragged_m_total(int64_t R, int E, int BM, int n_tiles) {
   return (int)(slots * (int64_t)n_tiles);
 }
 
+// A5: h = X_e W_gu[e]^T and a = silu(h_gate) h_up (h not stored when a.h is NULL).
+static hipError_t gateup_swiglu_bf16(const GroupedFfnArgs &a, const char *name, hipStream_t s) {
+  constexpr int BM = kGemmBM, BN = kGemmBN;
+  LaunchScope scope(name, s);
+  GemmParams p = base_params(a);
+  p.A = (const bf16_t *)a.x_perm;
+  p.B = (const bf16_t *)a.w_gu;
+  p.C = a.h;
+  p.C2 = (bf16_t *)a.a;
+  p.N = a.F;
+  p.K = a.d;
+  p.lda = a.d;
+  p.ldb = a.d;
+  p.ldc = 2 * (int64_t)a.F;
+  p.strideB = 2 * (int64_t)a.F * a.d;
+  p.n_tiles = (a.F + BN / 2 - 1) / (BN / 2);
+  p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
+  return run_dma<BM, BN, BM / 2, BN / 4, false, false, EPI_SWIGLU_FWD, false>(p, s);
+}
+
+hipError_t launch_ffn_recompute_bf16(const GroupedFfnArgs &a, hipStream_t s) {
+  return gateup_swiglu_bf16(a, "gg_gateup_recompute", s);
+}
+
 hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s) {
-  hipError_t err;
-  {
-    constexpr int BM = kGemmBM, BN = kGemmBN;
-    LaunchScope scope("gg_gateup_fwd", s);
-    GemmParams p = base_params(a);
-    p.A = (const bf16_t *)a.x_perm;
-    p.B = (const bf16_t *)a.w_gu;
-    p.C = a.h;
-    p.C2 = (bf16_t *)a.a;
-    p.N = a.F;
-    p.K = a.d;
-    p.lda = a.d;
-    p.ldb = a.d;
-    p.ldc = 2 * (int64_t)a.F;
-    p.strideB = 2 * (int64_t)a.F * a.d;
-    p.n_tiles = (a.F + BN / 2 - 1) / (BN / 2);
-    p.total = ragged_m_total(a.R, a.E, BM, p.n_tiles);
-    err = run_dma<BM, BN, BM / 2, BN / 4, false, false, EPI_SWIGLU_FWD, false>(p, s);
-  }
+  hipError_t err = gateup_swiglu_bf16(a, "gg_gateup_fwd", s);
   if (err != hipSuccess) return err;
   {
     constexpr int BM = kGemmBM, BN = kGemmBN;

@@ -101,10 +101,12 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParamsF p) {
   if (r >= m_valid || n >= p.N) return;
   if (EPI == F32_SWIGLU_FWD) {
     const int64_t row = crow0 + r;
-    p.C[row * p.ldc + n] = acc;
-    p.C[row * p.ldc + p.F + n] = acc_up;
+    if (p.C) {  // NULL when h is not kept
+      p.C[row * p.ldc + n] = acc;
+      p.C[row * p.ldc + p.F + n] = acc_up;
+    }
     p.C2[row * p.F + n] = silu_f(acc) * acc_up;
-  } else if (EPI == F32_SWIGLU_BWD) {
+  } else if (EPI == F32_SWIGLU_BWD) {  // p.C may equal p.H: each element is read, then written, by one thread
     const int64_t row = crow0 + r;
     const float hg = p.H[row * p.ldc + n];
     const float hu = p.H[row * p.ldc + p.F + n];
@@ -136,25 +138,31 @@ static GemmParamsF base_f(const GroupedFfnArgs &a) {
 
 static int ragged_total_f(int64_t R, int E, int n_tiles) { return (int)((R / kT + E) * (int64_t)n_tiles); }
 
+// h = X_e W_gu[e]^T and a = silu(h_gate) h_up (h not stored when a.h is NULL).
+static hipError_t gateup_swiglu_f32(const GroupedFfnArgs &a, const char *name, hipStream_t s) {
+  LaunchScope scope(name, s);
+  GemmParamsF p = base_f(a);
+  p.A = (const float *)a.x_perm;
+  p.B = (const float *)a.w_gu;
+  p.C = (float *)a.h;
+  p.C2 = (float *)a.a;
+  p.N = a.F;
+  p.K = a.d;
+  p.lda = a.d;
+  p.ldb = a.d;
+  p.ldc = 2 * (int64_t)a.F;
+  p.strideB = 2 * (int64_t)a.F * a.d;
+  p.n_tiles = (a.F + kT - 1) / kT;
+  p.total = ragged_total_f(a.R, a.E, p.n_tiles);
+  return run_f32<false, false, F32_SWIGLU_FWD, false>(p, s);
+}
+
+hipError_t launch_ffn_recompute_f32(const GroupedFfnArgs &a, hipStream_t s) {
+  return gateup_swiglu_f32(a, "gg_gateup_recompute_f32", s);
+}
+
 hipError_t launch_ffn_fwd_f32(const GroupedFfnArgs &a, hipStream_t s) {
-  hipError_t err;
-  {
-    LaunchScope scope("gg_gateup_fwd_f32", s);
-    GemmParamsF p = base_f(a);
-    p.A = (const float *)a.x_perm;
-    p.B = (const float *)a.w_gu;
-    p.C = (float *)a.h;
-    p.C2 = (float *)a.a;
-    p.N = a.F;
-    p.K = a.d;
-    p.lda = a.d;
-    p.ldb = a.d;
-    p.ldc = 2 * (int64_t)a.F;
-    p.strideB = 2 * (int64_t)a.F * a.d;
-    p.n_tiles = (a.F + kT - 1) / kT;
-    p.total = ragged_total_f(a.R, a.E, p.n_tiles);
-    err = run_f32<false, false, F32_SWIGLU_FWD, false>(p, s);
-  }
+  hipError_t err = gateup_swiglu_f32(a, "gg_gateup_fwd_f32", s);
   if (err != hipSuccess) return err;
   {
     LaunchScope scope("gg_down_fwd_f32", s);

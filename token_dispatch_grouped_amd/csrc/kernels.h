@@ -84,6 +84,10 @@ struct GroupedFfnArgs {
 hipError_t launch_ffn_fwd_bf16(const GroupedFfnArgs &a, hipStream_t s);
 hipError_t launch_ffn_bwd_bf16(const GroupedFfnArgs &a, hipStream_t s);
 hipError_t launch_ffn_fwd_f32(const GroupedFfnArgs &a, hipStream_t s);
+// Gate/up product + SwiGLU alone (h and a from x_perm), as in the forward;
+// used to recompute the activations at the start of a backward.
+hipError_t launch_ffn_recompute_bf16(const GroupedFfnArgs &a, hipStream_t s);
+hipError_t launch_ffn_recompute_f32(const GroupedFfnArgs &a, hipStream_t s);
 hipError_t launch_ffn_bwd_f32(const GroupedFfnArgs &a, hipStream_t s);
 
 }  // namespace moe

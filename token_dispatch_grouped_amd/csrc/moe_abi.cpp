@@ -202,9 +202,10 @@ moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, cons
   if (st != MOE_OK) return report(st, why);
   const moe_shape &s = *shape;
   if (s.T == 0) return MOE_OK;
+  const bool rc = (s.flags & MOE_FLAG_RECOMPUTE) != 0;
   const PtrArg args[] = {{"x_perm", x_perm, true, false}, {"w_gu", w_gu, true, false},
                          {"w_down", w_down, true, false}, {"offsets", offsets, true, false},
-                         {"h", h, true, false},           {"a", a, true, false},
+                         {"h", h, !rc, rc},               {"a", a, !rc, rc},
                          {"y", y, true, false}};
   st = validate_ptrs(args, 7, &why);
   if (st != MOE_OK) return report(st, why);
@@ -216,8 +217,8 @@ moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, cons
   fa.w_gu = w_gu;
   fa.w_down = w_down;
   fa.offsets = offsets;
-  fa.h = h;
-  fa.a = a;
+  fa.h = rc ? nullptr : h;  // NULL h: the gate/up epilogue writes only a
+  fa.a = rc ? ws : a;
   fa.y = y;
   hipStream_t hs = as_stream(stream);
   return hip_status(s.dtype == MOE_DTYPE_BF16 ? launch_ffn_fwd_bf16(fa, hs) : launch_ffn_fwd_f32(fa, hs),
@@ -300,8 +301,9 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
   if (st != MOE_OK) return report(st, why);
   const moe_shape &s = *shape;
   if (s.T == 0) return MOE_OK;
+  const bool rc = (s.flags & MOE_FLAG_RECOMPUTE) != 0;
   const PtrArg args[] = {{"dy", dy, true, false},         {"x_perm", x_perm, true, false},
-                         {"h", h, true, false},           {"a", a, true, false},
+                         {"h", h, !rc, rc},               {"a", a, !rc, rc},
                          {"w_gu", w_gu, true, false},     {"w_down", w_down, true, false},
                          {"offsets", offsets, true, false}, {"dx_perm", dx_perm, true, false},
                          {"dw_gu", dw_gu, true, false},   {"dw_down", dw_down, true, false}};
@@ -324,8 +326,17 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
   fa.dh = ws;
   fa.order = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + w.gemm_bwd_dh);
   hipStream_t hs = as_stream(stream);
-  return hip_status(s.dtype == MOE_DTYPE_BF16 ? launch_ffn_bwd_bf16(fa, hs) : launch_ffn_bwd_f32(fa, hs),
-                    "grouped_gemm_bwd");
+  const bool bf16 = s.dtype == MOE_DTYPE_BF16;
+  if (rc) {
+    // h and a again from x_perm; dH then overwrites h tile by tile (each
+    // workgroup of the dgrad reads the h tile it later writes, nobody else).
+    fa.h = ws;
+    fa.a = reinterpret_cast<char *>(ws) + w.gemm_bwd_dh + w.gemm_bwd_order;
+    st = hip_status(bf16 ? launch_ffn_recompute_bf16(fa, hs) : launch_ffn_recompute_f32(fa, hs),
+                    "grouped_gemm_bwd (recompute)");
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(bf16 ? launch_ffn_bwd_bf16(fa, hs) : launch_ffn_bwd_f32(fa, hs), "grouped_gemm_bwd");
 }
 
 moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const int32_t *row_of_slot,

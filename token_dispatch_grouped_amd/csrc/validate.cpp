@@ -22,7 +22,8 @@ moe_status validate_shape(const moe_shape *s, std::string *why) {
   if (s->k > s->E) return fail(why, MOE_ERR_INVALID_ARGUMENT, "k > E");
   if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16)
     return fail(why, MOE_ERR_UNSUPPORTED, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
-  if (s->flags & ~(uint32_t)MOE_FLAG_RENORM) return fail(why, MOE_ERR_UNSUPPORTED, "unknown flag bits");
+  if (s->flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_RECOMPUTE))
+    return fail(why, MOE_ERR_UNSUPPORTED, "unknown flag bits");
   if (s->E > 256) return fail(why, MOE_ERR_UNSUPPORTED, "E > 256");
   if (s->k > 16) return fail(why, MOE_ERR_UNSUPPORTED, "k > 16");
   if (s->d % 64 != 0 || s->F % 64 != 0) return fail(why, MOE_ERR_UNSUPPORTED, "d and F must be multiples of 64");
@@ -57,11 +58,14 @@ WorkspaceLayout workspace_layout(const moe_shape &s) {
   const int64_t nchunk = ceil_div(s.T, chunk_tokens);
   w.route_partial = align256((size_t)nchunk * (size_t)s.E * (size_t)s.d * 4);
   w.route_total = w.route_blk_cnt + w.route_partial;
-  w.gemm_fwd_total = 0;
   const size_t es = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
-  w.gemm_bwd_dh = align256((size_t)s.T * (size_t)s.k * 2 * (size_t)s.F * es);
+  const size_t R = (size_t)s.T * (size_t)s.k;
+  const bool recompute = (s.flags & MOE_FLAG_RECOMPUTE) != 0;
+  w.gemm_fwd_total = recompute ? align256(R * (size_t)s.F * es) : 0;
+  w.gemm_bwd_dh = align256(R * 2 * (size_t)s.F * es);
   w.gemm_bwd_order = align256((size_t)s.E * 4);
-  w.gemm_bwd_total = w.gemm_bwd_dh + w.gemm_bwd_order;
+  w.gemm_bwd_a = recompute ? align256(R * (size_t)s.F * es) : 0;
+  w.gemm_bwd_total = w.gemm_bwd_dh + w.gemm_bwd_order + w.gemm_bwd_a;
   return w;
 }
 

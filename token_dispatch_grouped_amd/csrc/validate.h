@@ -22,10 +22,11 @@ struct WorkspaceLayout {
   size_t route_blk_cnt;   // bytes of the per-workgroup expert histograms
   size_t route_partial;   // bytes of router weight-gradient partial sums
   size_t route_total;
-  size_t gemm_fwd_total;
-  size_t gemm_bwd_dh;     // bytes of dH
+  size_t gemm_fwd_total;  // recompute: a [R,F] at offset 0; else nothing
+  size_t gemm_bwd_dh;     // bytes of dH (recompute: the recomputed h first)
   size_t gemm_bwd_order;  // bytes of the expert order (int32 [E])
-  size_t gemm_bwd_total;
+  size_t gemm_bwd_a;      // recompute: bytes of the recomputed a; else 0
+  size_t gemm_bwd_total;  // dh | order | a
 };
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }

@@ -12,6 +12,11 @@ microbatch (``T_max``) and reused for any smaller one: microbatches of
 changing size, the empty one included, run on the same buffers ("buffer
 capacity transitions"). Weight gradients are fp32 and accumulate across
 calls; the caller zeroes them once.
+
+With ``recompute=True`` (MOE_FLAG_RECOMPUTE) the layer keeps no h or a
+buffers: the forward holds a in its workspace only and the backward
+recomputes h and a from x_perm. The same layer object also serves a
+forward with no backward after it (no-grad execution).
 """
 from __future__ import annotations
 
@@ -39,18 +44,19 @@ class Saved:
     row_of_slot: torch.Tensor
     src_of_row: torch.Tensor
     x_perm: torch.Tensor
-    h: torch.Tensor
-    a: torch.Tensor
+    h: Optional[torch.Tensor]  # None under recompute
+    a: Optional[torch.Tensor]  # None under recompute
     y: torch.Tensor
     out: torch.Tensor
 
 
 class MoeLayer:
     def __init__(self, T_max: int, d: int, E: int, k: int, F: int, dtype: int = L.MOE_DTYPE_BF16,
-                 renorm: bool = False, router: bool = False, device: str = "cuda"):
+                 renorm: bool = False, router: bool = False, recompute: bool = False, device: str = "cuda"):
         self.T_max, self.d, self.E, self.k, self.F = T_max, d, E, k, F
         self.dtype = dtype
-        self.flags = L.MOE_FLAG_RENORM if renorm else 0
+        self.recompute = recompute
+        self.flags = (L.MOE_FLAG_RENORM if renorm else 0) | (L.MOE_FLAG_RECOMPUTE if recompute else 0)
         self.router = router
         dev = torch.device(device)
         td = torch_dtype(dtype)
@@ -70,8 +76,8 @@ class MoeLayer:
         self.row_of_slot = torch.empty(T_max, k, dtype=i32, device=dev)
         self.src_of_row = torch.empty(R, dtype=i32, device=dev)
         self.x_perm = torch.empty(R, d, dtype=td, device=dev)
-        self.h = torch.empty(R, 2 * F, dtype=td, device=dev)
-        self.a = torch.empty(R, F, dtype=td, device=dev)
+        self.h = None if recompute else torch.empty(R, 2 * F, dtype=td, device=dev)
+        self.a = None if recompute else torch.empty(R, F, dtype=td, device=dev)
         self.y = torch.empty(R, d, dtype=td, device=dev)
         self.out = torch.empty(T_max, d, dtype=td, device=dev)
         # backward
@@ -88,7 +94,8 @@ class MoeLayer:
     def saved(self, T: int) -> Saved:
         R = T * self.k
         return Saved(T, self.logits[:T], self.topk_idx[:T], self.topk_w[:T], self.counts, self.offsets,
-                     self.row_of_slot[:T], self.src_of_row[:R], self.x_perm[:R], self.h[:R], self.a[:R],
+                     self.row_of_slot[:T], self.src_of_row[:R], self.x_perm[:R],
+                     None if self.h is None else self.h[:R], None if self.a is None else self.a[:R],
                      self.y[:R], self.out[:T])
 
     # ------------------------------------------------------------------
@@ -128,6 +135,15 @@ class MoeLayer:
         return dict(dy=self.dy[:R], dtopk_w=self.dtopk_w[:T], dlogits=self.dlogits[:T], dx_perm=self.dx_perm[:R],
                     dx=self.dx[:T], dh=self.dh_view(T),
                     dx_router=self.dx_router[:T] if use_router else None)
+
+    def fwd_a_view(self, T: int) -> torch.Tensor:
+        """Under recompute: a of the last forward, read from the forward
+        workspace (valid until the next forward)."""
+        assert self.recompute, "a lives in the forward workspace only under recompute"
+        R = T * self.k
+        td = torch_dtype(self.dtype)
+        es = 2 if td == torch.bfloat16 else 4
+        return self.fwd_ws[: R * self.F * es].view(td).view(R, self.F)
 
     def dh_view(self, T: int) -> torch.Tensor:
         """dH of the last backward, read from the backward workspace."""

@@ -98,6 +98,17 @@ class Workload:
     def microbatches(self) -> tuple:
         return self.micro_T if self.micro_T is not None else (self.T,)
 
+    def flops_fwd(self, T: Optional[int] = None) -> float:
+        """Algorithmic FLOPs of one forward pass (grouped GEMMs, plus the
+        router GEMM when it runs)."""
+        ts = (T,) if T is not None else self.microbatches
+        fl = 0.0
+        for t in ts:
+            fl += 6.0 * t * self.k * self.d * self.F
+            if self.routing == "router":
+                fl += 2.0 * t * self.d * self.E
+        return fl
+
     def flops_fwd_bwd(self, T: Optional[int] = None) -> float:
         """Algorithmic FLOPs of one forward+backward pass (grouped GEMMs only,
         plus the router GEMM when it runs)."""
