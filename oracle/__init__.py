@@ -6,8 +6,12 @@ and the bench's ``cpu_baseline`` leg use it. It shares no code with the HIP
 library and imports nothing from it.
 
 Everything is plain NumPy in float64, written to be checked by eye against
-the layer's definition; see ``oracle.moe`` for the functions and the passages
-each one follows.
+the layer's definition; see ``oracle.moe`` for the layer's functions,
+``oracle.optim`` for the optimizer update, and the passages each one follows.
 """
 from .moe import *  # noqa: F401,F403
-from .moe import __all__  # noqa: F401
+from .moe import __all__ as _moe_all
+from .optim import *  # noqa: F401,F403
+from .optim import __all__ as _optim_all
+
+__all__ = list(_moe_all) + list(_optim_all)
