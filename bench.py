@@ -19,6 +19,10 @@ the algorithmic rate (the recompute product is extra work the method does not
 need) and ``executed_tflops`` counts it. ``--mode nograd`` times the forward
 alone under MOE_FLAG_RECOMPUTE (no activations kept), value = 6*R*d*F per
 step over its time. The default (``train``) is the headline measurement.
+``--optimizer`` appends the fused AdamW update of both expert weight tensors
+(fp32 masters and moments, bf16 working copies written in place, gradients
+zeroed in the same pass) to every training step; its kernel is reported as
+``adamw`` with 34 bytes per weight element.
 """
 from __future__ import annotations
 
@@ -106,6 +110,8 @@ def parse():
     ap.add_argument("--mode", choices=("train", "recompute", "nograd"), default="train",
                     help="train: forward+backward keeping h and a (default); recompute: forward+backward with "
                          "MOE_FLAG_RECOMPUTE; nograd: forward alone with MOE_FLAG_RECOMPUTE")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="append the fused AdamW update of the expert weights to every step (train/recompute)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes before timing (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -207,6 +213,10 @@ def main():
     torch.cuda.synchronize()
 
     nograd = args.mode == "nograd"
+    opt = None
+    if args.optimizer and not nograd:
+        from token_dispatch_grouped_amd.optim import ExpertAdamW
+        opt = ExpertAdamW([wgu, wdn], lr=1e-5, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
 
     def step():
         for mb in mbs:
@@ -214,6 +224,8 @@ def main():
             layer.forward(T, mb["x"], wgu, wdn, logits=mb["logits"], w_router=wr, bias=bias)
             if not nograd:
                 layer.backward(T, mb["dout"], wgu, wdn, dw_gu, dw_dn, x=mb["x"], w_router=wr, dw_router=dw_r)
+        if opt is not None:
+            opt.step([dw_gu, dw_dn], grad_scale=1.0 / len(mbs), zero_grad=True)
 
     if args.calibrate_copy > 0:
         src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device=dev).fill_(1)
@@ -264,6 +276,11 @@ def main():
             by = sum(mem_bytes(name, mb["T"], w.d, w.k, s, router) for mb in mbs)
             gbps = by / (ms / args.steps * 1e-3) / 1e9
             entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
+        elif name == "adamw":
+            # theta, grad, m, v read; theta, m, v, bf16 copy, zeroed grad written
+            by = 3 * w.E * w.F * w.d * (28 + (2 if w.dtype == BF16 else 0) + 4)
+            gbps = by / (ms / args.steps * 1e-3) / 1e9
+            entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
         kernels[name] = entry
 
     gemm_names = [n for n in kernels if n.replace("_f32", "") in GEMM_KERNELS]
@@ -298,6 +315,7 @@ def main():
                                 if args.mode == "recompute" else 0.0)
     cfg = {"workload": w.name, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d, "E_local": w.E,
            "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "mode": args.mode,
+           "optimizer": "adamw" if opt is not None else None,
            "description": w.description}
     line = {
         "metric": METRIC_NOGRAD if nograd else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -236,6 +236,45 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
 moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const int32_t *row_of_slot,
                            const float *dx_extra, void *dx, moe_stream_t stream);
 
+/*
+ * Optimizer update of the expert weights (the "optimizer update" step the
+ * canary of Support combined expert and data parallelism in TrainerRank,
+ * Acceptance, completes after forward and backward). The pages do not name
+ * the optimizer; this is AdamW (Adam with decoupled weight decay), computed
+ * element by element on fp32 master weights as PyTorch's AdamW does:
+ *   g     = grad_scale * grad
+ *   m     = beta1 m + (1 - beta1) g            (exp_avg, fp32, in place)
+ *   v     = beta2 v + (1 - beta2) g^2          (exp_avg_sq, fp32, in place)
+ *   param = param (1 - lr weight_decay)
+ *           - lr / (1 - beta1^step) * m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ * If param_bf16 is non-NULL, the updated param rounded to bf16 (nearest-even)
+ * is also written there, e.g. straight into the w_gu / w_down the grouped
+ * GEMMs read. With MOE_ADAMW_ZERO_GRAD, grad is set to zero in the same pass,
+ * ready for the next accumulation. grad_scale turns the summed gradients of
+ * several microbatches into a mean if the caller wants one.
+ * All arrays hold n elements, contiguous, 16-byte aligned, not overlapping;
+ * n == 0 is a no-op that accepts NULLs. The update of an element reads and
+ * writes that element only: results do not depend on n or on launch layout.
+ * Errors: cfg NULL, lr < 0, a beta outside [0, 1), eps <= 0, weight_decay < 0,
+ * a non-finite scalar, step < 1 or n < 0 -> MOE_ERR_INVALID_ARGUMENT; unknown
+ * flag bits or n >= 2^40 -> MOE_ERR_UNSUPPORTED.
+ */
+enum { MOE_ADAMW_ZERO_GRAD = 1u };
+
+typedef struct moe_adamw_config {
+  float lr;           /* learning rate */
+  float beta1;        /* first-moment decay */
+  float beta2;        /* second-moment decay */
+  float eps;          /* added to the bias-corrected sqrt(v) */
+  float weight_decay; /* decoupled weight decay */
+  float grad_scale;   /* gradient multiplier applied first */
+  int64_t step;       /* step number of this update, 1 for the first */
+  uint32_t flags;     /* MOE_ADAMW_* */
+} moe_adamw_config;
+
+moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, float *grad,
+                          float *exp_avg, float *exp_avg_sq, void *param_bf16, moe_stream_t stream);
+
 /* Static English text for a status code. */
 const char *moe_status_string(moe_status status);
 

@@ -181,6 +181,47 @@ def test_workspace_monotone_in_T(dtype):
     assert prev[2] >= R * 2 * 1408 * es
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(lr=-1e-3), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(beta1=1.0), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(beta2=-0.1), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(eps=0.0), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(weight_decay=-0.5), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(grad_scale=float("inf")), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(lr=float("nan")), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(step=0), L.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_adamw_config_validation(kw, status):
+    args = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, grad_scale=1.0, step=1)
+    args.update(kw)
+    cfg = L.make_adamw_config(**args)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_adamw_step(cfg, 16, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == status
+
+
+def test_adamw_argument_rules():
+    cfg = L.make_adamw_config(1e-3)
+    moe.moe_adamw_step(cfg, 0, None, None, None, None, None, stream=0)  # n == 0: no-op, NULLs accepted
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_adamw_step(cfg, -1, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_adamw_step(cfg, 1 << 40, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_adamw_step(cfg, 16, FAKE, None, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "grad" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_adamw_step(cfg, 16, FAKE, FAKE, FAKE, FAKE, FAKE + 8, stream=0)
+    assert ei.value.status == L.MOE_ERR_MISALIGNED
+    bad = L.make_adamw_config(1e-3)
+    bad.flags = 2
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_adamw_step(bad, 16, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
 def test_validation_built_alone_with_asan(tmp_path):
     """The validation unit is plain C++: build it with g++ (no HIP) and
@@ -214,6 +255,13 @@ int main() {
   expect(validate_ptrs(nul, 1, &why), MOE_ERR_INVALID_ARGUMENT, "null");
   PtrArg must[] = {{"a", &x, false, true}};
   expect(validate_ptrs(must, 1, &why), MOE_ERR_INVALID_ARGUMENT, "must be null");
+  moe_adamw_config ac{1e-3f, 0.9f, 0.999f, 1e-8f, 0.01f, 1.f, 1, 0};
+  expect(validate_adamw(&ac, 100, &why), MOE_OK, "adamw ok");
+  expect(validate_adamw(nullptr, 100, &why), MOE_ERR_INVALID_ARGUMENT, "adamw null");
+  moe_adamw_config ab = ac; ab.step = 0; expect(validate_adamw(&ab, 100, &why), MOE_ERR_INVALID_ARGUMENT, "step 0");
+  ab = ac; ab.beta2 = 1.f; expect(validate_adamw(&ab, 100, &why), MOE_ERR_INVALID_ARGUMENT, "beta2 1");
+  ab = ac; ab.flags = 8; expect(validate_adamw(&ab, 100, &why), MOE_ERR_UNSUPPORTED, "adamw flag");
+  expect(validate_adamw(&ac, (int64_t)1 << 40, &why), MOE_ERR_UNSUPPORTED, "adamw n");
   expect(validate_workspace(nullptr, 0, 0, &why), MOE_OK, "no ws needed");
   expect(validate_workspace(nullptr, 0, 16, &why), MOE_ERR_WORKSPACE, "ws null");
   expect(validate_workspace((void*)0x1000, 8, 16, &why), MOE_ERR_WORKSPACE, "ws short");

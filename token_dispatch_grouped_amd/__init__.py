@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     moe_workspace_size, moe_route, moe_permute, moe_grouped_gemm_fwd, moe_unpermute_combine,
     moe_unpermute_combine_bwd, moe_route_bwd, moe_grouped_gemm_bwd, moe_permute_bwd, moe_status_string,
     moe_last_error, moe_version, moe_profiler_enable, moe_profiler_reset, moe_profiler_read_all,
+    MOE_ADAMW_ZERO_GRAD, make_adamw_config, moe_adamw_config, moe_adamw_step,
 )
 
-__all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "load", "make_shape"]
+__all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "load", "make_shape",
+                                                                  "make_adamw_config"]

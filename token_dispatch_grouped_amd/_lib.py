@@ -40,6 +40,14 @@ class moe_shape(ctypes.Structure):
 
 
 _P = ctypes.c_void_p
+class moe_adamw_config(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("grad_scale", ctypes.c_float),
+                ("step", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+
+
+MOE_ADAMW_ZERO_GRAD = 1
+
 _S = ctypes.POINTER(moe_shape)
 _SZ = ctypes.c_size_t
 
@@ -53,6 +61,7 @@ _SIGNATURES = {
     "moe_route_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
+    "moe_adamw_step": (ctypes.c_int, [ctypes.POINTER(moe_adamw_config), ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_profiler_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -183,6 +192,19 @@ def moe_permute_bwd(shape, dx_perm, row_of_slot, dx_extra, dx, stream=None):
     lib = load()
     _check(lib.moe_permute_bwd(ctypes.byref(shape), ptr(dx_perm), ptr(row_of_slot), ptr(dx_extra), ptr(dx),
                                _stream(stream)), "moe_permute_bwd")
+
+
+def make_adamw_config(lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                      weight_decay: float = 0.01, grad_scale: float = 1.0, step: int = 1,
+                      zero_grad: bool = False) -> moe_adamw_config:
+    return moe_adamw_config(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                            float(grad_scale), int(step), MOE_ADAMW_ZERO_GRAD if zero_grad else 0)
+
+
+def moe_adamw_step(cfg, n, param, grad, exp_avg, exp_avg_sq, param_bf16=None, stream=None):
+    lib = load()
+    _check(lib.moe_adamw_step(ctypes.byref(cfg), int(n), ptr(param), ptr(grad), ptr(exp_avg), ptr(exp_avg_sq),
+                              ptr(param_bf16), _stream(stream)), "moe_adamw_step")
 
 
 def moe_status_string(status: int) -> str:

@@ -90,4 +90,15 @@ hipError_t launch_ffn_recompute_bf16(const GroupedFfnArgs &a, hipStream_t s);
 hipError_t launch_ffn_recompute_f32(const GroupedFfnArgs &a, hipStream_t s);
 hipError_t launch_ffn_bwd_f32(const GroupedFfnArgs &a, hipStream_t s);
 
+// Fused AdamW step (optim.hip). Scalars are prepared on the host: decay =
+// 1 - lr*wd, step_size = lr / (1 - b1^t), bc2_sqrt = sqrt(1 - b2^t).
+struct AdamwLaunch {
+  float *theta, *grad, *m, *v;
+  void *lowp;  // bf16 copy of theta, or NULL
+  int64_t n;
+  float b1, b2, decay, step_size, bc2_sqrt, eps, scale;
+  bool zero_grad;
+};
+hipError_t launch_adamw(const AdamwLaunch &a, hipStream_t s);
+
 }  // namespace moe

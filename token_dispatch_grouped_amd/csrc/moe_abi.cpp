@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -353,6 +354,40 @@ moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const in
   return hip_status(launch_permute_bwd(dx_perm, row_of_slot, dx_extra, dx, s.T, s.d, s.k, s.dtype == MOE_DTYPE_BF16,
                                        as_stream(stream)),
                     "permute_bwd");
+}
+
+moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, float *grad, float *exp_avg,
+                          float *exp_avg_sq, void *param_bf16, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_adamw(cfg, n, &why);
+  if (st != MOE_OK) return report(st, why);
+  if (n == 0) return MOE_OK;
+  const PtrArg args[] = {{"param", param, true, false},     {"grad", grad, true, false},
+                         {"exp_avg", exp_avg, true, false}, {"exp_avg_sq", exp_avg_sq, true, false},
+                         {"param_bf16", param_bf16, false, false}};
+  st = validate_ptrs(args, 5, &why);
+  if (st != MOE_OK) return report(st, why);
+  // bias corrections in double, then rounded once to fp32
+  const double bc1 = 1.0 - std::pow((double)cfg->beta1, (double)cfg->step);
+  const double bc2 = 1.0 - std::pow((double)cfg->beta2, (double)cfg->step);
+  if (!(bc1 > 0.0) || !(bc2 > 0.0))
+    return report(MOE_ERR_INVALID_ARGUMENT, "bias correction underflows to zero (beta too close to 0 at this step?)");
+  AdamwLaunch a;
+  a.theta = param;
+  a.grad = grad;
+  a.m = exp_avg;
+  a.v = exp_avg_sq;
+  a.lowp = param_bf16;
+  a.n = n;
+  a.b1 = cfg->beta1;
+  a.b2 = cfg->beta2;
+  a.decay = (float)(1.0 - (double)cfg->lr * (double)cfg->weight_decay);
+  a.step_size = (float)((double)cfg->lr / bc1);
+  a.bc2_sqrt = (float)std::sqrt(bc2);
+  a.eps = cfg->eps;
+  a.scale = cfg->grad_scale;
+  a.zero_grad = (cfg->flags & MOE_ADAMW_ZERO_GRAD) != 0;
+  return hip_status(launch_adamw(a, as_stream(stream)), "adamw_step");
 }
 
 moe_status moe_profiler_enable(int on) {

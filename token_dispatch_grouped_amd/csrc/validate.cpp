@@ -5,6 +5,8 @@
 // is consumed (review note on Add MoE expert parallel training runtime).
 #include "validate.h"
 
+#include <cmath>
+
 #include <stdio.h>
 
 namespace moe {
@@ -102,6 +104,23 @@ moe_status validate_workspace(const void *ws, size_t have, size_t need, std::str
     snprintf(buf, sizeof buf, "workspace too small: %zu bytes given, %zu needed", have, need);
     return fail(why, MOE_ERR_WORKSPACE, buf);
   }
+  return MOE_OK;
+}
+
+moe_status validate_adamw(const moe_adamw_config *c, int64_t n, std::string *why) {
+  if (!c) return fail(why, MOE_ERR_INVALID_ARGUMENT, "adamw config is NULL");
+  if (n < 0) return fail(why, MOE_ERR_INVALID_ARGUMENT, "negative element count");
+  if (n >= ((int64_t)1 << 40)) return fail(why, MOE_ERR_UNSUPPORTED, "element count >= 2^40");
+  if (c->flags & ~(uint32_t)MOE_ADAMW_ZERO_GRAD) return fail(why, MOE_ERR_UNSUPPORTED, "unknown adamw flag bits");
+  const float vals[] = {c->lr, c->beta1, c->beta2, c->eps, c->weight_decay, c->grad_scale};
+  for (float v : vals)
+    if (!std::isfinite(v)) return fail(why, MOE_ERR_INVALID_ARGUMENT, "non-finite adamw scalar");
+  if (c->lr < 0.f) return fail(why, MOE_ERR_INVALID_ARGUMENT, "lr < 0");
+  if (c->beta1 < 0.f || c->beta1 >= 1.f || c->beta2 < 0.f || c->beta2 >= 1.f)
+    return fail(why, MOE_ERR_INVALID_ARGUMENT, "beta outside [0, 1)");
+  if (c->eps <= 0.f) return fail(why, MOE_ERR_INVALID_ARGUMENT, "eps <= 0");
+  if (c->weight_decay < 0.f) return fail(why, MOE_ERR_INVALID_ARGUMENT, "weight_decay < 0");
+  if (c->step < 1) return fail(why, MOE_ERR_INVALID_ARGUMENT, "step < 1");
   return MOE_OK;
 }
 

@@ -50,6 +50,9 @@ struct PtrArg {
 };
 moe_status validate_ptrs(const PtrArg *args, int n, std::string *why);
 
+// AdamW scalars and element count (see moe_adamw_step).
+moe_status validate_adamw(const moe_adamw_config *cfg, int64_t n, std::string *why);
+
 // Workspace check: NULL or short -> MOE_ERR_WORKSPACE (a zero requirement
 // accepts anything).
 moe_status validate_workspace(const void *ws, size_t have, size_t need, std::string *why);
