@@ -110,6 +110,9 @@ def parse():
     ap.add_argument("--mode", choices=("train", "recompute", "nograd"), default="train",
                     help="train: forward+backward keeping h and a (default); recompute: forward+backward with "
                          "MOE_FLAG_RECOMPUTE; nograd: forward alone with MOE_FLAG_RECOMPUTE")
+    ap.add_argument("--aux", action="store_true",
+                    help="add the auxiliary losses (load balancing 0.01, router z-loss 0.001) and routing metrics "
+                         "to the forward and their gradient to the backward")
     ap.add_argument("--optimizer", action="store_true",
                     help="append the fused AdamW update of the expert weights to every step (train/recompute)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -197,7 +200,7 @@ def main():
     router = w.routing == "router"
     Tmax = max(max(w.microbatches), 1)
     layer = MoeLayer(Tmax, w.d, w.E, w.k, w.F, dt, renorm=args.renorm, router=router,
-                     recompute=args.mode != "train")
+                     recompute=args.mode != "train", aux=(0.01, 1e-3) if args.aux else None)
     W = inp["weights"]
     wgu, wdn = dev_t(W["w_gu"], w.dtype), dev_t(W["w_down"], w.dtype)
     wr = dev_t(W["w_router"], w.dtype) if router else None
@@ -315,7 +318,7 @@ def main():
                                 if args.mode == "recompute" else 0.0)
     cfg = {"workload": w.name, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d, "E_local": w.E,
            "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "mode": args.mode,
-           "optimizer": "adamw" if opt is not None else None,
+           "optimizer": "adamw" if opt is not None else None, "aux_losses": bool(args.aux),
            "description": w.description}
     line = {
         "metric": METRIC_NOGRAD if nograd else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

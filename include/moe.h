@@ -82,7 +82,11 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  * a from x_perm into its workspace (one more gate/up product, bit-identical
  * to the forward's), then writes dH over the recomputed h. Results equal
  * those without the flag bit for bit. */
-enum { MOE_FLAG_RENORM = 1u, MOE_FLAG_RECOMPUTE = 2u };
+enum { MOE_FLAG_RENORM = 1u, MOE_FLAG_RECOMPUTE = 2u, MOE_FLAG_ACCUMULATE_DLOGITS = 4u };
+/* MOE_FLAG_ACCUMULATE_DLOGITS: moe_route_bwd adds the routing-weight
+ * gradient to what dlogits already holds (typically the auxiliary losses'
+ * gradient from moe_aux_loss) instead of overwriting it, and with a router
+ * back-propagates the sum into dx_router and dw_router. */
 
 typedef struct moe_shape {
   int64_t T;      /* tokens in this microbatch (>= 0) */
@@ -99,7 +103,7 @@ typedef void *moe_stream_t;
 
 /*
  * Workspace sizes in bytes for a shape: route_ws serves moe_route and
- * moe_route_bwd, gemm_fwd_ws serves moe_grouped_gemm_fwd and gemm_bwd_ws
+ * moe_route_bwd and moe_aux_loss, gemm_fwd_ws serves moe_grouped_gemm_fwd and gemm_bwd_ws
  * serves moe_grouped_gemm_bwd. A workspace sized for some T serves every
  * smaller T of the same (d, E, k, F, dtype), so one buffer sized for the
  * largest microbatch can be reused across microbatches of any size
@@ -197,6 +201,8 @@ moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dout, c
  *   dw_router += dlogits^T x       [E,d] fp32 (accumulated; zero it once),
  * both required; otherwise x, dx_router and dw_router must be NULL. The
  * router weight gradient is reduced in a fixed order (no atomics).
+ * With MOE_FLAG_ACCUMULATE_DLOGITS the result is added to dlogits (and the
+ * router backward, if any, uses the sum).
  * ws: route workspace of at least route_ws bytes.
  */
 moe_status moe_route_bwd(const moe_shape *shape, const float *dtopk_w, const float *logits,
@@ -235,6 +241,52 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
  */
 moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const int32_t *row_of_slot,
                            const float *dx_extra, void *dx, moe_stream_t stream);
+
+/*
+ * MoE auxiliary losses and routing metrics ("MoE losses" and "MoE metrics",
+ * Add MoE expert parallel training runtime, Summary and Testing; the pages
+ * name them without a definition). From the fp32 logits [T,E] of a
+ * microbatch and the counts [E] moe_route produced, with p the softmax over
+ * all E experts (whatever MOE_FLAG_RENORM says):
+ *   f_e   = counts[e] / (T k),   P_e = (1/T) sum_t p[t,e]
+ *   L_bal = E sum_e f_e P_e      load balancing (Switch Transformers, 2.2)
+ *   L_z   = (1/T) sum_t lse_t^2, lse_t = log sum_e exp(logits[t,e])
+ *                                router z-loss (ST-MoE, 3.1)
+ * losses [2] fp32 (NULL: not written) receives (L_bal, L_z), unweighted.
+ * metrics [MOE_METRIC_SCALARS + 2E] fp32 (NULL: not written) receives the
+ * scalars indexed by MOE_METRIC_*, then f_e for every e, then P_e.
+ * dlogits [T,E] fp32 (NULL: not written) receives the gradient of
+ *   balance_coef L_bal + z_coef L_z
+ * with respect to the logits, f held constant (it is piecewise constant):
+ *   dlogits[t,i] = p_i (G_i - sum_e p_e G_e) + (2 z_coef / T) lse_t p_i,
+ *   G_e = balance_coef E f_e / T,
+ * overwriting dlogits, or added to it with MOE_AUX_ACCUMULATE. To train a
+ * router through moe_route_bwd, call this first and set
+ * MOE_FLAG_ACCUMULATE_DLOGITS on the shape. Every token needs a finite
+ * logit. All sums run in a fixed order (no atomics). T == 0 writes nothing.
+ * ws: route workspace of at least route_ws bytes.
+ * Errors: cfg NULL or a non-finite coefficient -> MOE_ERR_INVALID_ARGUMENT;
+ * unknown cfg flag bits -> MOE_ERR_UNSUPPORTED.
+ */
+enum { MOE_AUX_ACCUMULATE = 1u };
+enum {
+  MOE_METRIC_IMBALANCE = 0,     /* max_e counts[e] / (T k / E) */
+  MOE_METRIC_EMPTY_EXPERTS = 1, /* experts with no rows */
+  MOE_METRIC_COUNT_CV = 2,      /* population std / mean of counts */
+  MOE_METRIC_ENTROPY = 3,       /* mean over tokens of -sum_e p log p (nats) */
+  MOE_METRIC_MAX_PROB = 4,      /* mean over tokens of max_e p */
+  MOE_METRIC_SCALARS = 5        /* number of scalars before the per-expert arrays */
+};
+
+typedef struct moe_aux_config {
+  float balance_coef; /* weight of L_bal in the gradient */
+  float z_coef;       /* weight of L_z in the gradient */
+  uint32_t flags;     /* MOE_AUX_* */
+} moe_aux_config;
+
+moe_status moe_aux_loss(const moe_shape *shape, const float *logits, const int32_t *counts,
+                        const moe_aux_config *cfg, float *losses, float *metrics, float *dlogits,
+                        void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * Optimizer update of the expert weights (the "optimizer update" step the

@@ -60,7 +60,7 @@ def shape(T=64, d=64, E=4, k=2, F=128, dtype=L.MOE_DTYPE_BF16, flags=0):
     (dict(E=257, k=2), L.MOE_ERR_UNSUPPORTED),
     (dict(E=32, k=17), L.MOE_ERR_UNSUPPORTED),
     (dict(dtype=7), L.MOE_ERR_UNSUPPORTED),
-    (dict(flags=4), L.MOE_ERR_UNSUPPORTED),              # unknown flag bit
+    (dict(flags=8), L.MOE_ERR_UNSUPPORTED),              # unknown flag bit
     (dict(T=2 ** 28, E=8, k=8), L.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
 ])
 def test_shape_validation(kw, status):
@@ -220,6 +220,35 @@ def test_adamw_argument_rules():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_adamw_step(bad, 16, FAKE, FAKE, FAKE, FAKE, None, stream=0)
     assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
+def test_aux_loss_argument_rules():
+    s = shape(T=300, E=16, k=4)
+    route_ws, _, _ = moe.moe_workspace_size(s)
+    ok = L.make_aux_config(0.01, 1e-3)
+    # T == 0, or nothing requested: no-op with NULLs
+    moe.moe_aux_loss(shape(T=0, E=16, k=4), None, None, ok, None, None, None, None, 0, stream=0)
+    moe.moe_aux_loss(s, None, None, ok, None, None, None, None, 0, stream=0)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_aux_loss(s, FAKE, FAKE, L.make_aux_config(float("nan"), 0.0), FAKE, None, None, FAKE, route_ws,
+                         stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    bad = L.make_aux_config(0.01, 0.0)
+    bad.flags = 4
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_aux_loss(s, FAKE, FAKE, bad, FAKE, None, None, FAKE, route_ws, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_aux_loss(s, FAKE, None, ok, FAKE, None, None, FAKE, route_ws, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "counts" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_aux_loss(s, FAKE, FAKE, ok, FAKE, None, None, None, 0, stream=0)
+    assert ei.value.status == L.MOE_ERR_WORKSPACE
+    # the route workspace covers the auxiliary pass at any T
+    for T in (1, 255, 256, 257, 32768, 1 << 20):
+        rw, _, _ = moe.moe_workspace_size(shape(T=T, E=256, k=8, d=64, F=64))
+        blocks = -(-T // max(256, (-(-T // 1024) + 3) // 4 * 4))
+        assert rw >= blocks * (256 + 3) * 4
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")

@@ -10,7 +10,10 @@ from ._lib import (  # noqa: F401
     moe_unpermute_combine_bwd, moe_route_bwd, moe_grouped_gemm_bwd, moe_permute_bwd, moe_status_string,
     moe_last_error, moe_version, moe_profiler_enable, moe_profiler_reset, moe_profiler_read_all,
     MOE_ADAMW_ZERO_GRAD, make_adamw_config, moe_adamw_config, moe_adamw_step,
+    MOE_FLAG_ACCUMULATE_DLOGITS, MOE_AUX_ACCUMULATE, MOE_METRIC_IMBALANCE, MOE_METRIC_EMPTY_EXPERTS,
+    MOE_METRIC_COUNT_CV, MOE_METRIC_ENTROPY, MOE_METRIC_MAX_PROB, MOE_METRIC_SCALARS, make_aux_config,
+    moe_aux_config, moe_aux_loss,
 )
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "load", "make_shape",
-                                                                  "make_adamw_config"]
+                                                                  "make_adamw_config", "make_aux_config"]

@@ -26,6 +26,10 @@ MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_FLAG_RENORM = 1
 MOE_FLAG_RECOMPUTE = 2
+MOE_FLAG_ACCUMULATE_DLOGITS = 4
+MOE_AUX_ACCUMULATE = 1
+MOE_METRIC_IMBALANCE, MOE_METRIC_EMPTY_EXPERTS, MOE_METRIC_COUNT_CV, MOE_METRIC_ENTROPY, MOE_METRIC_MAX_PROB = range(5)
+MOE_METRIC_SCALARS = 5
 
 
 class MoeError(RuntimeError):
@@ -48,6 +52,10 @@ class moe_adamw_config(ctypes.Structure):
 
 MOE_ADAMW_ZERO_GRAD = 1
 
+
+class moe_aux_config(ctypes.Structure):
+    _fields_ = [("balance_coef", ctypes.c_float), ("z_coef", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
 _S = ctypes.POINTER(moe_shape)
 _SZ = ctypes.c_size_t
 
@@ -61,6 +69,7 @@ _SIGNATURES = {
     "moe_route_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
+    "moe_aux_loss": (ctypes.c_int, [_S, _P, _P, ctypes.POINTER(moe_aux_config), _P, _P, _P, _P, _SZ, _P]),
     "moe_adamw_step": (ctypes.c_int, [ctypes.POINTER(moe_adamw_config), ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -192,6 +201,16 @@ def moe_permute_bwd(shape, dx_perm, row_of_slot, dx_extra, dx, stream=None):
     lib = load()
     _check(lib.moe_permute_bwd(ctypes.byref(shape), ptr(dx_perm), ptr(row_of_slot), ptr(dx_extra), ptr(dx),
                                _stream(stream)), "moe_permute_bwd")
+
+
+def make_aux_config(balance_coef: float, z_coef: float, accumulate: bool = False) -> moe_aux_config:
+    return moe_aux_config(float(balance_coef), float(z_coef), MOE_AUX_ACCUMULATE if accumulate else 0)
+
+
+def moe_aux_loss(shape, logits, counts, cfg, losses, metrics, dlogits, ws, ws_bytes, stream=None):
+    lib = load()
+    _check(lib.moe_aux_loss(ctypes.byref(shape), ptr(logits), ptr(counts), ctypes.byref(cfg), ptr(losses),
+                            ptr(metrics), ptr(dlogits), ptr(ws), int(ws_bytes), _stream(stream)), "moe_aux_loss")
 
 
 def make_adamw_config(lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,

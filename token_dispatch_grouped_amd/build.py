@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["moe_abi.cpp", "validate.cpp", "route.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip", "optim.hip"]
+SOURCES = ["moe_abi.cpp", "validate.cpp", "route.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip", "optim.hip", "aux.hip"]
 ARCH = "gfx950"
 
 

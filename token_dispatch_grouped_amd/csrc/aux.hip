@@ -1,0 +1,214 @@
+// MoE auxiliary losses and routing metrics (latency-bound, two launches).
+//
+// Pass 1 (aux_partial_kernel): one wavefront per token, lanes across experts
+// (lane l holds experts l, l+64, l+128, l+192). Per token it forms the full
+// softmax p and lse = log sum exp(logits), adds p into per-lane sums of
+// P_e, lse^2, the entropy -sum p log p (log p taken as logit - lse) and the
+// top probability (= exp(max - lse)), and, if asked, writes the gradient
+//   dlogits[t,i] = p_i (G_i - sum_e p_e G_e) + (2 beta / T) lse p_i,
+//   G_e = alpha E counts[e] / (T^2 k)     (d(alpha L_bal)/dp[t,e])
+// overwriting or adding to dlogits. Each workgroup covers a contiguous run
+// of tokens, its four wavefronts taking every fourth token; their sums are
+// combined in a fixed order into one partial row [E + 3] per workgroup.
+// Pass 2 (aux_finalize_kernel, one workgroup): partial rows summed in
+// workgroup order, count statistics, losses and the metrics array.
+// No atomics: results are the same run to run.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kAuxThreads = 256;
+constexpr int kAuxMaxE = 256;
+constexpr int kAuxPerLane = kAuxMaxE / kWave;  // experts per lane
+constexpr int kAuxScalars = 3;                 // entropy, lse^2, top probability
+
+MOE_DEVICE float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float *__restrict__ logits,
+                                                                  const int32_t *__restrict__ counts,
+                                                                  float *__restrict__ partial, float *dlogits,
+                                                                  int64_t T, int E, int tokens_per_block,
+                                                                  float gscale, float zscale, int accumulate) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * tokens_per_block;
+  int64_t t_end = t0 + tokens_per_block;
+  if (t_end > T) t_end = T;
+  float G[kAuxPerLane], psum[kAuxPerLane];
+#pragma unroll
+  for (int q = 0; q < kAuxPerLane; ++q) {
+    const int e = lane + kWave * q;
+    G[q] = (dlogits && e < E) ? gscale * (float)counts[e] : 0.f;
+    psum[q] = 0.f;
+  }
+  float ent = 0.f, zz = 0.f, mx = 0.f;
+  for (int64_t t = t0 + wv; t < t_end; t += kAuxThreads / kWave) {
+    const float *row = logits + t * E;
+    float l[kAuxPerLane];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kAuxPerLane; ++q) {
+      const int e = lane + kWave * q;
+      l[q] = e < E ? row[e] : -INFINITY;
+      m = fmaxf(m, l[q]);
+    }
+    m = wave_max(m);
+    float ex[kAuxPerLane], s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kAuxPerLane; ++q) {
+      ex[q] = expf(l[q] - m);  // 0 for -inf and for lanes past E
+      s += ex[q];
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+    const float lse = m + logf(s);
+    float p[kAuxPerLane], plogp = 0.f, pg = 0.f;
+#pragma unroll
+    for (int q = 0; q < kAuxPerLane; ++q) {
+      p[q] = ex[q] * inv;
+      if (p[q] > 0.f) plogp += p[q] * (l[q] - lse);
+      pg += p[q] * G[q];
+      psum[q] += p[q];
+    }
+    ent -= wave_sum(plogp);
+    zz += lse * lse;
+    mx += inv;  // the top probability is exp(m - lse) = 1 / s
+    if (dlogits) {
+      pg = wave_sum(pg);
+      float *drow = dlogits + t * E;
+#pragma unroll
+      for (int q = 0; q < kAuxPerLane; ++q) {
+        const int e = lane + kWave * q;
+        if (e < E) {
+          const float v = p[q] * (G[q] - pg) + zscale * lse * p[q];
+          drow[e] = accumulate ? drow[e] + v : v;
+        }
+      }
+    }
+  }
+  __shared__ float sp[kAuxThreads / kWave][kAuxMaxE];
+  __shared__ float ss[kAuxThreads / kWave][kAuxScalars];
+#pragma unroll
+  for (int q = 0; q < kAuxPerLane; ++q) {
+    const int e = lane + kWave * q;
+    if (e < E) sp[wv][e] = psum[q];
+  }
+  if (lane == 0) {
+    ss[wv][0] = ent;
+    ss[wv][1] = zz;
+    ss[wv][2] = mx;
+  }
+  __syncthreads();
+  float *out = partial + (int64_t)blockIdx.x * (E + kAuxScalars);
+  for (int e = threadIdx.x; e < E; e += kAuxThreads) out[e] = ((sp[0][e] + sp[1][e]) + sp[2][e]) + sp[3][e];
+  if (threadIdx.x < kAuxScalars) {
+    const int i = threadIdx.x;
+    out[E + i] = ((ss[0][i] + ss[1][i]) + ss[2][i]) + ss[3][i];
+  }
+}
+
+// Fixed-order tree sum over the 256 threads of the workgroup.
+MOE_DEVICE float block_sum_256(float v, float *red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = kAuxThreads / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+MOE_DEVICE float block_max_256(float v, float *red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = kAuxThreads / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(const float *__restrict__ partial, int nblk,
+                                                                   const int32_t *__restrict__ counts, int64_t T,
+                                                                   int E, int k, float *losses, float *metrics) {
+  __shared__ float red[kAuxThreads];
+  const int e = threadIdx.x;  // E <= 256: one expert per thread
+  const int ld = E + kAuxScalars;
+  const float Tf = (float)T;
+  const float rows = (float)((double)T * k);
+  const float mean = (float)((double)T * k / E);
+  float fP = 0.f, dev2 = 0.f, cmax = 0.f, empty = 0.f;
+  if (e < E) {
+    float P = 0.f;
+    for (int b = 0; b < nblk; ++b) P += partial[(int64_t)b * ld + e];
+    P /= Tf;
+    const float c = (float)counts[e];
+    const float f = c / rows;
+    fP = f * P;
+    dev2 = (c - mean) * (c - mean);
+    cmax = c;
+    empty = counts[e] == 0 ? 1.f : 0.f;
+    if (metrics) {
+      metrics[MOE_METRIC_SCALARS + e] = f;
+      metrics[MOE_METRIC_SCALARS + E + e] = P;
+    }
+  }
+  float sc = 0.f;
+  if (e < kAuxScalars)
+    for (int b = 0; b < nblk; ++b) sc += partial[(int64_t)b * ld + E + e];
+  const float sum_fP = block_sum_256(fP, red);
+  const float sum_dev2 = block_sum_256(dev2, red);
+  const float sum_empty = block_sum_256(empty, red);
+  const float max_c = block_max_256(cmax, red);
+  // scalars from threads 0..2 -> shared
+  __shared__ float scal[kAuxScalars];
+  if (e < kAuxScalars) scal[e] = sc / Tf;
+  __syncthreads();
+  if (e == 0) {
+    if (losses) {
+      losses[0] = (float)E * sum_fP;
+      losses[1] = scal[1];
+    }
+    if (metrics) {
+      metrics[MOE_METRIC_IMBALANCE] = max_c / mean;
+      metrics[MOE_METRIC_EMPTY_EXPERTS] = sum_empty;
+      metrics[MOE_METRIC_COUNT_CV] = sqrtf(sum_dev2 / (float)E) / mean;
+      metrics[MOE_METRIC_ENTROPY] = scal[0];
+      metrics[MOE_METRIC_MAX_PROB] = scal[2];
+    }
+  }
+}
+
+hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *losses, float *metrics, float *dlogits,
+                           float *partial, int64_t T, int E, int k, float alpha, float beta, bool accumulate,
+                           hipStream_t s) {
+  const int tpb = aux_tokens_per_block(T);
+  const int nblk = (int)((T + tpb - 1) / tpb);
+  const float gscale = (float)((double)alpha * E / ((double)T * (double)T * k));
+  const float zscale = (float)(2.0 * beta / (double)T);
+  {
+    LaunchScope scope("aux_partial", s);
+    aux_partial_kernel<<<nblk, kAuxThreads, 0, s>>>(logits, counts, partial, dlogits, T, E, tpb, gscale, zscale,
+                                                     accumulate ? 1 : 0);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || (!losses && !metrics)) return err;
+  {
+    LaunchScope scope("aux_finalize", s);
+    aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(partial, nblk, counts, T, E, k, losses, metrics);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -46,7 +46,7 @@ hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, i
                         int64_t T, int E, int k, bool renorm, hipStream_t s);
 hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
                             const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
-                            hipStream_t s);
+                            bool accumulate, hipStream_t s);
 hipError_t launch_router_bwd(const float *dlogits, const void *x, const void *w_router, float *dx_router,
                              float *dw_router, float *partial, int64_t T, int d, int E, bool bf16,
                              hipStream_t s);
@@ -100,5 +100,11 @@ struct AdamwLaunch {
   bool zero_grad;
 };
 hipError_t launch_adamw(const AdamwLaunch &a, hipStream_t s);
+
+// Auxiliary losses and routing metrics (aux.hip); partial: the route
+// workspace, at least route_aux bytes.
+hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *losses, float *metrics, float *dlogits,
+                           float *partial, int64_t T, int E, int k, float alpha, float beta, bool accumulate,
+                           hipStream_t s);
 
 }  // namespace moe

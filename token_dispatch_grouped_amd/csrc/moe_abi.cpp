@@ -284,7 +284,8 @@ moe_status moe_route_bwd(const moe_shape *shape, const float *dtopk_w, const flo
   }
   hipStream_t hs = as_stream(stream);
   st = hip_status(launch_route_bwd(dtopk_w, logits, topk_idx, topk_w, dlogits, s.T, s.E, s.k,
-                                   (s.flags & MOE_FLAG_RENORM) != 0, hs),
+                                   (s.flags & MOE_FLAG_RENORM) != 0, (s.flags & MOE_FLAG_ACCUMULATE_DLOGITS) != 0,
+                                   hs),
                   "route_bwd");
   if (st != MOE_OK || !router) return st;
   float *partial = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + w.route_blk_cnt);
@@ -354,6 +355,30 @@ moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const in
   return hip_status(launch_permute_bwd(dx_perm, row_of_slot, dx_extra, dx, s.T, s.d, s.k, s.dtype == MOE_DTYPE_BF16,
                                        as_stream(stream)),
                     "permute_bwd");
+}
+
+moe_status moe_aux_loss(const moe_shape *shape, const float *logits, const int32_t *counts,
+                        const moe_aux_config *cfg, float *losses, float *metrics, float *dlogits, void *ws,
+                        size_t ws_bytes, moe_stream_t stream) {
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  st = validate_aux(cfg, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0 || (!losses && !metrics && !dlogits)) return MOE_OK;
+  const PtrArg args[] = {{"logits", logits, true, false},  {"counts", counts, true, false},
+                         {"losses", losses, false, false}, {"metrics", metrics, false, false},
+                         {"dlogits", dlogits, false, false}};
+  st = validate_ptrs(args, 5, &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(s);
+  st = validate_workspace(ws, ws_bytes, w.route_aux, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(launch_aux_loss(logits, counts, losses, metrics, dlogits, static_cast<float *>(ws), s.T, s.E, s.k,
+                                    cfg->balance_coef, cfg->z_coef, (cfg->flags & MOE_AUX_ACCUMULATE) != 0,
+                                    as_stream(stream)),
+                    "aux_loss");
 }
 
 moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, float *grad, float *exp_avg,

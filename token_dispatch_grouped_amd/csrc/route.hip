@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict_
                                                         const int32_t *__restrict__ topk_idx,
                                                         const float *__restrict__ topk_w,
                                                         float *__restrict__ dlogits, int64_t ntok, int E, int k,
-                                                        int renorm) {
+                                                        int renorm, int accumulate) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= ntok) return;
   const float *row = logits + t * E;
@@ -288,12 +288,17 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict_
     }
   }
   if (renorm) {
-    for (int e = 0; e < E; ++e) drow[e] = 0.f;
+    if (!accumulate)
+      for (int e = 0; e < E; ++e) drow[e] = 0.f;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k) drow[ids[j]] = w[j] * (g[j] - s);
+      if (j < k) drow[ids[j]] = accumulate ? drow[ids[j]] + w[j] * (g[j] - s) : w[j] * (g[j] - s);
     return;
   }
+  // accumulate: what dlogits held at the selected ids, before the first pass
+  float base[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) base[j] = (accumulate && j < k) ? drow[ids[j]] : 0.f;
   float m = -INFINITY;
   for (int e = 0; e < E; ++e) {
     float l = row[e];
@@ -308,14 +313,14 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict_
   for (int e = 0; e < E; ++e) {
     float l = row[e];
     float p = (l == l) ? expf(l - m) * inv : 0.f;
-    drow[e] = -p * s;
+    drow[e] = accumulate ? drow[e] - p * s : -p * s;
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < k) {
       float l = row[ids[j]];
       float p = (l == l) ? expf(l - m) * inv : 0.f;
-      drow[ids[j]] = p * (g[j] - s);
+      drow[ids[j]] = accumulate ? base[j] + p * (g[j] - s) : p * (g[j] - s);
     }
   }
 }
@@ -435,18 +440,18 @@ hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, i
 
 hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
                             const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
-                            hipStream_t s) {
+                            bool accumulate, hipStream_t s) {
   LaunchScope scope("route_bwd", s);
   dim3 grid((unsigned)((T + 255) / 256));
-  const int r = renorm ? 1 : 0;
+  const int r = renorm ? 1 : 0, a = accumulate ? 1 : 0;
   if (k <= 2)
-    route_bwd_kernel<2><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+    route_bwd_kernel<2><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   else if (k <= 4)
-    route_bwd_kernel<4><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+    route_bwd_kernel<4><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   else if (k <= 8)
-    route_bwd_kernel<8><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+    route_bwd_kernel<8><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   else
-    route_bwd_kernel<16><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r);
+    route_bwd_kernel<16><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ moe_status validate_shape(const moe_shape *s, std::string *why) {
   if (s->k > s->E) return fail(why, MOE_ERR_INVALID_ARGUMENT, "k > E");
   if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16)
     return fail(why, MOE_ERR_UNSUPPORTED, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
-  if (s->flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_RECOMPUTE))
+  if (s->flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_RECOMPUTE | MOE_FLAG_ACCUMULATE_DLOGITS))
     return fail(why, MOE_ERR_UNSUPPORTED, "unknown flag bits");
   if (s->E > 256) return fail(why, MOE_ERR_UNSUPPORTED, "E > 256");
   if (s->k > 16) return fail(why, MOE_ERR_UNSUPPORTED, "k > 16");
@@ -59,7 +59,10 @@ WorkspaceLayout workspace_layout(const moe_shape &s) {
   if (chunk_tokens < 256) chunk_tokens = 256;
   const int64_t nchunk = ceil_div(s.T, chunk_tokens);
   w.route_partial = align256((size_t)nchunk * (size_t)s.E * (size_t)s.d * 4);
+  const int64_t aux_blocks = ceil_div(s.T, aux_tokens_per_block(s.T));
+  w.route_aux = align256((size_t)aux_blocks * ((size_t)s.E + 3) * 4);
   w.route_total = w.route_blk_cnt + w.route_partial;
+  if (w.route_aux > w.route_total) w.route_total = w.route_aux;
   const size_t es = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
   const size_t R = (size_t)s.T * (size_t)s.k;
   const bool recompute = (s.flags & MOE_FLAG_RECOMPUTE) != 0;
@@ -121,6 +124,14 @@ moe_status validate_adamw(const moe_adamw_config *c, int64_t n, std::string *why
   if (c->eps <= 0.f) return fail(why, MOE_ERR_INVALID_ARGUMENT, "eps <= 0");
   if (c->weight_decay < 0.f) return fail(why, MOE_ERR_INVALID_ARGUMENT, "weight_decay < 0");
   if (c->step < 1) return fail(why, MOE_ERR_INVALID_ARGUMENT, "step < 1");
+  return MOE_OK;
+}
+
+moe_status validate_aux(const moe_aux_config *c, std::string *why) {
+  if (!c) return fail(why, MOE_ERR_INVALID_ARGUMENT, "aux config is NULL");
+  if (c->flags & ~(uint32_t)MOE_AUX_ACCUMULATE) return fail(why, MOE_ERR_UNSUPPORTED, "unknown aux flag bits");
+  if (!std::isfinite(c->balance_coef) || !std::isfinite(c->z_coef))
+    return fail(why, MOE_ERR_INVALID_ARGUMENT, "non-finite aux coefficient");
   return MOE_OK;
 }
 

@@ -17,10 +17,12 @@ constexpr int kRouterChunksMax = 32;    // router weight-gradient partial sums
 constexpr int kGemmBM = 256;            // bf16 grouped GEMM rows per tile
 constexpr int kGemmBN = 256;            // bf16 grouped GEMM columns per tile
 constexpr int kGemmF32Tile = 16;        // fp32 grouped GEMM tile edge
+constexpr int kAuxMaxBlocks = 1024;     // partial rows of the auxiliary-loss pass
 
 struct WorkspaceLayout {
   size_t route_blk_cnt;   // bytes of the per-workgroup expert histograms
   size_t route_partial;   // bytes of router weight-gradient partial sums
+  size_t route_aux;       // bytes of the auxiliary-loss partial rows (shares the route workspace)
   size_t route_total;
   size_t gemm_fwd_total;  // recompute: a [R,F] at offset 0; else nothing
   size_t gemm_bwd_dh;     // bytes of dH (recompute: the recomputed h first)
@@ -31,6 +33,14 @@ struct WorkspaceLayout {
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tokens per workgroup of the auxiliary-loss pass: at least 256, at most
+// kAuxMaxBlocks workgroups, a multiple of 4 (one token per wavefront in turn).
+inline int aux_tokens_per_block(int64_t T) {
+  int64_t tpb = ceil_div(T, kAuxMaxBlocks);
+  if (tpb < 256) tpb = 256;
+  return (int)((tpb + 3) / 4 * 4);
+}
 
 // Validates the shape alone. On failure writes a message to *why.
 moe_status validate_shape(const moe_shape *s, std::string *why);
@@ -52,6 +62,9 @@ moe_status validate_ptrs(const PtrArg *args, int n, std::string *why);
 
 // AdamW scalars and element count (see moe_adamw_step).
 moe_status validate_adamw(const moe_adamw_config *cfg, int64_t n, std::string *why);
+
+// Auxiliary-loss coefficients and flags (see moe_aux_loss).
+moe_status validate_aux(const moe_aux_config *cfg, std::string *why);
 
 // Workspace check: NULL or short -> MOE_ERR_WORKSPACE (a zero requirement
 // accepts anything).

@@ -17,6 +17,12 @@ With ``recompute=True`` (MOE_FLAG_RECOMPUTE) the layer keeps no h or a
 buffers: the forward holds a in its workspace only and the backward
 recomputes h and a from x_perm. The same layer object also serves a
 forward with no backward after it (no-grad execution).
+
+With ``aux=(balance_coef, z_coef)`` the forward also computes the auxiliary
+losses (load balancing, router z-loss) and the routing metrics into
+``aux_losses`` / ``metrics``, and the backward adds the losses' gradient to
+dlogits before the routing-weight gradient (MOE_FLAG_ACCUMULATE_DLOGITS), so
+a router trains on both.
 """
 from __future__ import annotations
 
@@ -52,11 +58,14 @@ class Saved:
 
 class MoeLayer:
     def __init__(self, T_max: int, d: int, E: int, k: int, F: int, dtype: int = L.MOE_DTYPE_BF16,
-                 renorm: bool = False, router: bool = False, recompute: bool = False, device: str = "cuda"):
+                 renorm: bool = False, router: bool = False, recompute: bool = False, aux=None,
+                 device: str = "cuda"):
         self.T_max, self.d, self.E, self.k, self.F = T_max, d, E, k, F
         self.dtype = dtype
         self.recompute = recompute
-        self.flags = (L.MOE_FLAG_RENORM if renorm else 0) | (L.MOE_FLAG_RECOMPUTE if recompute else 0)
+        self.aux = None if aux is None else (float(aux[0]), float(aux[1]))
+        self.flags = ((L.MOE_FLAG_RENORM if renorm else 0) | (L.MOE_FLAG_RECOMPUTE if recompute else 0)
+                      | (L.MOE_FLAG_ACCUMULATE_DLOGITS if aux is not None else 0))
         self.router = router
         dev = torch.device(device)
         td = torch_dtype(dtype)
@@ -87,6 +96,9 @@ class MoeLayer:
         self.dx_perm = torch.empty(R, d, dtype=td, device=dev)
         self.dx = torch.empty(T_max, d, dtype=td, device=dev)
         self.dx_router = torch.empty(T_max, d, dtype=f32, device=dev) if router else None
+        # auxiliary losses (L_bal, L_z) and routing metrics of the last forward
+        self.aux_losses = torch.zeros(2, dtype=f32, device=dev) if aux is not None else None
+        self.metrics = torch.zeros(L.MOE_METRIC_SCALARS + 2 * E, dtype=f32, device=dev) if aux is not None else None
 
     def shape(self, T: int) -> L.moe_shape:
         return L.make_shape(T, self.d, self.E, self.k, self.F, self.dtype, self.flags)
@@ -112,6 +124,9 @@ class MoeLayer:
         logits buffer unless a router weight is given."""
         s = self.shape(T)
         self.route(T, x=x, logits=logits, w_router=w_router, bias=bias, stream=stream)
+        if self.aux is not None:
+            L.moe_aux_loss(s, self.logits, self.counts, L.make_aux_config(*self.aux), self.aux_losses, self.metrics,
+                           None, self.route_ws, self.route_ws.numel(), stream)
         L.moe_permute(s, x, self.row_of_slot, self.x_perm, stream)
         L.moe_grouped_gemm_fwd(s, self.x_perm, w_gu, w_down, self.offsets, self.h, self.a, self.y, self.fwd_ws,
                                self.fwd_ws.numel(), stream)
@@ -124,6 +139,9 @@ class MoeLayer:
         s = self.shape(T)
         L.moe_unpermute_combine_bwd(s, dout, self.y, self.topk_w, self.row_of_slot, self.dy, self.dtopk_w, stream)
         use_router = w_router is not None
+        if self.aux is not None:  # aux gradient first; moe_route_bwd then adds to it
+            L.moe_aux_loss(s, self.logits, self.counts, L.make_aux_config(*self.aux), None, None, self.dlogits,
+                           self.route_ws, self.route_ws.numel(), stream)
         L.moe_route_bwd(s, self.dtopk_w, self.logits, self.topk_idx, self.topk_w, x if use_router else None,
                         w_router, self.dlogits, self.dx_router if use_router else None,
                         dw_router if use_router else None, self.route_ws, self.route_ws.numel(), stream)
