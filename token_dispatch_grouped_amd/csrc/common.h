@@ -68,6 +68,11 @@ template <> struct Elem<bf16_t> {
 MOE_DEVICE u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 MOE_DEVICE void st16(void *p, const u32x4_t &v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 
+// Non-temporal 16-byte load: for data read once.
+MOE_DEVICE u32x4_t ld16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
 // Non-temporal 16-byte store: for streams written once and read much later.
 MOE_DEVICE void st16_nt(void *p, const u32x4_t &v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
