@@ -146,3 +146,34 @@ def test_layer_router_with_aux_losses():
     assert_close("dx_router", to_host64(g["dx_router"]), dxr, tol)
     assert_close("dw_router", to_host64(dwr), dwr_ref, tol)
     assert_close("dx", to_host64(g["dx"]), go["dx"] + dxr, tol)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_layer_logits_with_aux_losses(renorm):
+    """Given-logits mode (the 32k workloads' mode) with the auxiliary losses:
+    dlogits = routing-weight gradient (plain or renormalised) + aux gradient,
+    summed by moe_route_bwd under MOE_FLAG_ACCUMULATE_DLOGITS."""
+    import torch
+    import token_dispatch_grouped_amd as m
+    from token_dispatch_grouped_amd.layer import MoeLayer
+    w = small_workload(777, 128, 16, 4, 128, BF16, "zipf", seed=71, n_empty=2)
+    inp = make_inputs(w)
+    W, mb = inp["weights"], inp["micro"][0]
+    alpha, beta = 0.05, 2e-3
+    layer = MoeLayer(777, w.d, w.E, w.k, w.F, m.MOE_DTYPE_BF16, renorm=renorm, aux=(alpha, beta))
+    wgu, wdn = to_device(W["w_gu"], BF16), to_device(W["w_down"], BF16)
+    dgu = torch.zeros(w.E, 2 * w.F, w.d, device="cuda")
+    ddn = torch.zeros(w.E, w.d, w.F, device="cuda")
+    layer.forward(777, to_device(mb["x"], BF16), wgu, wdn, logits=to_device(mb["logits"], F32))
+    g = layer.backward(777, to_device(mb["dout"], BF16), wgu, wdn, dgu, ddn)
+    torch.cuda.synchronize()
+    lg = mb["logits"].astype(np.float64)
+    wgu64, wdn64 = to_f64(W["w_gu"], BF16), to_f64(W["w_down"], BF16)
+    _, svo = oracle.layer_fwd(to_f64(mb["x"], BF16), wgu64, wdn64, w.k, logits=lg, renorm=renorm)
+    go = oracle.layer_bwd(to_f64(mb["dout"], BF16), svo, wgu64, wdn64, renorm=renorm)
+    total = go["dlogits"] + oracle.aux_losses_grad(lg, svo["counts"], w.k, alpha, beta)
+    assert_close("dlogits (routing + aux)", to_host64(g["dlogits"]), total, TOL[BF16])
+    assert_close("dx", to_host64(g["dx"]), go["dx"], TOL[BF16])
+    lb, lz = oracle.aux_losses(lg, svo["counts"], w.k)
+    assert_close("L_bal", to_host64(layer.aux_losses[0:1]), np.array([lb]), TOL_F32)
+    assert_close("L_z", to_host64(layer.aux_losses[1:2]), np.array([lz]), TOL_F32)
