@@ -8,10 +8,11 @@ accumulating in fp32). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. ``value`` is the layer's algorithmic TFLOP/s
 (18*R*d*F per step, R = T*k routed rows, plus 6*T*d*E when the router GEMM
-runs) over the stream time of the timed steps. ``roofline`` describes the
-dominant kernel, timed with HIP events on the launch stream inside the timed
-region; ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the
-same workload on this host's cores.
+runs) over the stream time of K timed steps. A second run of K steps brackets
+every kernel with HIP events on its launch stream: the per-kernel table and
+``roofline`` (the dominant kernel) come from it. ``cpu_baseline`` is the
+fp64 oracle timed on a bounded sample of the same workload on this host's
+cores.
 
 ``--mode recompute`` runs the same step with MOE_FLAG_RECOMPUTE (no h/a kept
 between forward and backward; the backward recomputes them): ``value`` stays
@@ -243,20 +244,29 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    moe.moe_profiler_reset()
-    moe.moe_profiler_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    moe.moe_profiler_enable(False)
+
+    def timed(profile):
+        """K steps between a synchronize and HIP events on the launch stream;
+        with profile, every kernel is also bracketed by events of its own."""
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        moe.moe_profiler_reset()
+        moe.moe_profiler_enable(profile)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        moe.moe_profiler_enable(False)
+        return ev0.elapsed_time(ev1), wall_s
+
+    # the step rate without instrumentation, then the same K steps with the
+    # per-kernel events (whose recording adds a little time of its own)
+    stream_ms, wall = timed(False)
+    prof_ms, _ = timed(True)
     kern = moe.moe_profiler_read_all()
-    stream_ms = ev0.elapsed_time(ev1)
     ms_per_step = stream_ms / args.steps
 
     flops_step = w.flops_fwd() if nograd else w.flops_fwd_bwd()
@@ -332,6 +342,7 @@ def main():
         "permute_combine_pct_hbm": round(100 * pc_gbps / PEAK_HBM_GBPS, 2),
         "executed_tflops": round(executed_fl / (ms_per_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
+        "ms_per_step_with_kernel_events": round(prof_ms / args.steps, 4),
         "input_gen_s": round(t_gen, 2),
         "kernels": kernels,
         "roofline": roof,
