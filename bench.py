@@ -57,16 +57,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "d88eef1400cf41d39804cdf33603b4402b5d77eb6e36a3e399eb736a23b6406d",
+    "sources_sha256": "27b649edf3729cc3db1666a1c5f8a6ccd2e224c34ebc882a963709ba5396ca6f",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (5.738 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.188 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.162 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (6.025 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (4.373 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (11.506 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (5.570 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.190 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.173 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.997 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.372 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (11.574 + 0.645) * 2 ** 30,
     },
 }
 
