@@ -35,6 +35,12 @@ There is no capacity factor: every (token, expert) pair is computed, so an
 expert may receive any number of rows including zero. Gradients are plain
 sums (no averaging); the weight gradients of several microbatches add up.
 
+Every function below stays in float64 from start to finish. Where the GPU
+path rounds intermediates to the layer dtype (H, A, Y, dY, dH, dX_perm are
+stored in bf16 for a bf16 layer; sums are rounded once), nothing on the pages
+fixes those rounding points: agreement there is parity unpinned beyond the
+stated tolerance.
+
 Selection compares logits, not probabilities: exp() can merge distinct
 logits into equal probabilities, comparing logits cannot. NaN ranks below
 -inf; -0.0 and +0.0 are equal (a tie).
