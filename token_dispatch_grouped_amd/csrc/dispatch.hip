@@ -25,24 +25,30 @@ namespace moe {
 // grouped GEMM reads next.
 
 // A4: x_perm[row_of_slot[t,j]] = x[t]. Each source chunk is read once and
-// written k times.
+// written k times; a thread copies chunks c and c + nc/2 of one token (nc is
+// even: d is a multiple of 64), which keeps twice the stores in flight.
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void permute_kernel(const T *__restrict__ x, const int32_t *__restrict__ ros,
                                                       T *__restrict__ xp, int64_t ntok, int nc, int k) {
   const int64_t nrows = ntok * k;
   constexpr int V = Elem<T>::kVec;
+  const int half = nc / 2;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = g / nc;
-  const int c = (int)(g - t * nc);
+  const int64_t t = g / half;
+  const int c = (int)(g - t * half);
   if (t >= ntok) return;
   const int64_t ld = (int64_t)nc * V;
   int64_t row[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) row[j] = j < k ? ros[t * k + j] : -1;
-  const u32x4_t v = ld16(x + t * ld + (int64_t)c * V);
+  const u32x4_t v0 = ld16(x + t * ld + (int64_t)c * V);
+  const u32x4_t v1 = ld16(x + t * ld + (int64_t)(c + half) * V);
 #pragma unroll
   for (int j = 0; j < KMAX; ++j)
-    if (j < k && (uint64_t)row[j] < (uint64_t)nrows) st16(xp + row[j] * ld + (int64_t)c * V, v);
+    if (j < k && (uint64_t)row[j] < (uint64_t)nrows) {
+      st16(xp + row[j] * ld + (int64_t)c * V, v0);
+      st16(xp + row[j] * ld + (int64_t)(c + half) * V, v1);
+    }
 }
 
 // A7: out[t] = sum_j w[t,j] y[row_of_slot[t,j]].
@@ -206,7 +212,7 @@ static void permute_t(const void *x, const int32_t *ros, void *xp, int64_t T_, i
   const int nc = d / Elem<T>::kVec;
   with_kmax(k, [&](auto km) {
     constexpr int KM = decltype(km)::value;
-    permute_kernel<T, KM><<<blocks_for(T_ * nc), 256, 0, s>>>((const T *)x, ros, (T *)xp, T_, nc, k);
+    permute_kernel<T, KM><<<blocks_for(T_ * (nc / 2)), 256, 0, s>>>((const T *)x, ros, (T *)xp, T_, nc, k);
   });
 }
 
