@@ -122,6 +122,16 @@ def parse():
     return ap.parse_args()
 
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, target_s, fwd_only=False):
     """Time the fp64 oracle (as it is) on the first T_s tokens of the first
     microbatch: one forward+backward (forward alone if fwd_only), T_s sized
@@ -328,7 +338,7 @@ def main():
     # the recompute product is work done beyond the method's own FLOPs
     executed_fl = flops_step + (GEMM_KERNELS["gg_gateup_recompute"] * sum(mb["T"] for mb in mbs) * w.k * w.d * w.F
                                 if args.mode == "recompute" else 0.0)
-    cfg = {"workload": w.name, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d, "E_local": w.E,
+    cfg = {"workload": w.name, "seed": w.seed, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d, "E_local": w.E,
            "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "mode": args.mode,
            "optimizer": "adamw" if opt is not None else None, "aux_losses": bool(args.aux),
            "description": w.description}
@@ -345,6 +355,8 @@ def main():
         "executed_tflops": round(executed_fl / (ms_per_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
         "ms_per_step_with_kernel_events": round(prof_ms / args.steps, 4),
+        "device_memory_GB": round(torch.cuda.max_memory_allocated(dev) / 1e9, 2),
+        "host_cpu": host_cpu_model(),
         "input_gen_s": round(t_gen, 2),
         "kernels": kernels,
         "roofline": roof,

@@ -15,11 +15,22 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "moe.h"
 #include "kernels.h"
 #include "validate.h"
 
 namespace moe {
+
+// A roctx range around each C-ABI call, so that a marker trace shows the
+// calls above their kernels (rocprofv3 --marker-trace). Costs nothing
+// measurable when no tool listens.
+struct AbiRange {
+  explicit AbiRange(const char *name) { roctxRangePushA(name); }
+  ~AbiRange() { roctxRangePop(); }
+};
+
 
 static thread_local std::string g_last_error;
 
@@ -136,6 +147,7 @@ moe_status moe_workspace_size(const moe_shape *shape, size_t *route_ws, size_t *
 moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router, const float *bias, float *logits,
                      int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *row_of_slot,
                      int32_t *src_of_row, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  moe::AbiRange range("moe_route");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -174,6 +186,7 @@ moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router
 
 moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *row_of_slot, void *x_perm,
                        moe_stream_t stream) {
+  moe::AbiRange range("moe_permute");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -198,6 +211,7 @@ static GroupedFfnArgs ffn_args(const moe_shape &s) {
 moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, const void *w_gu, const void *w_down,
                                 const int32_t *offsets, void *h, void *a, void *y, void *ws, size_t ws_bytes,
                                 moe_stream_t stream) {
+  moe::AbiRange range("moe_grouped_gemm_fwd");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -228,6 +242,7 @@ moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, cons
 
 moe_status moe_unpermute_combine(const moe_shape *shape, const void *y, const float *topk_w,
                                  const int32_t *row_of_slot, void *out, moe_stream_t stream) {
+  moe::AbiRange range("moe_unpermute_combine");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -244,6 +259,7 @@ moe_status moe_unpermute_combine(const moe_shape *shape, const void *y, const fl
 
 moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dout, const void *y, const float *topk_w,
                                      const int32_t *row_of_slot, void *dy, float *dtopk_w, moe_stream_t stream) {
+  moe::AbiRange range("moe_unpermute_combine_bwd");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -262,6 +278,7 @@ moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dout, c
 moe_status moe_route_bwd(const moe_shape *shape, const float *dtopk_w, const float *logits, const int32_t *topk_idx,
                          const float *topk_w, const void *x, const void *w_router, float *dlogits, float *dx_router,
                          float *dw_router, void *ws, size_t ws_bytes, moe_stream_t stream) {
+  moe::AbiRange range("moe_route_bwd");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -298,6 +315,7 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
                                 const void *a, const void *w_gu, const void *w_down, const int32_t *offsets,
                                 void *dx_perm, float *dw_gu, float *dw_down, void *ws, size_t ws_bytes,
                                 moe_stream_t stream) {
+  moe::AbiRange range("moe_grouped_gemm_bwd");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -343,6 +361,7 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
 
 moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const int32_t *row_of_slot,
                            const float *dx_extra, void *dx, moe_stream_t stream) {
+  moe::AbiRange range("moe_permute_bwd");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -360,6 +379,7 @@ moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const in
 moe_status moe_aux_loss(const moe_shape *shape, const float *logits, const int32_t *counts,
                         const moe_aux_config *cfg, float *losses, float *metrics, float *dlogits, void *ws,
                         size_t ws_bytes, moe_stream_t stream) {
+  moe::AbiRange range("moe_aux_loss");
   std::string why;
   moe_status st = validate_shape(shape, &why);
   if (st != MOE_OK) return report(st, why);
@@ -383,6 +403,7 @@ moe_status moe_aux_loss(const moe_shape *shape, const float *logits, const int32
 
 moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, float *grad, float *exp_avg,
                           float *exp_avg_sq, void *param_bf16, moe_stream_t stream) {
+  moe::AbiRange range("moe_adamw_step");
   std::string why;
   moe_status st = validate_adamw(cfg, n, &why);
   if (st != MOE_OK) return report(st, why);
