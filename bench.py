@@ -61,12 +61,12 @@ TRAFFIC = {
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (5.570 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.190 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.173 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.997 + 0.322) * 2 ** 30,
+        "gg_gateup_fwd": (5.516 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.189 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.200 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.975 + 0.322) * 2 ** 30,
         "gg_gateup_dgrad": (4.372 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (11.574 + 0.645) * 2 ** 30,
+        "gg_gateup_wgrad": (11.545 + 0.645) * 2 ** 30,
     },
 }
 
