@@ -57,7 +57,7 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "27b649edf3729cc3db1666a1c5f8a6ccd2e224c34ebc882a963709ba5396ca6f",
+    "sources_sha256": "aa3656da2d43eb500797539135576688d59bcbe47323e3ab0236b959cf4f91fd",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30

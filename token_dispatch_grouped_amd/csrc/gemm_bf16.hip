@@ -301,7 +301,7 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
   }
 }
 
-constexpr int kGroupM = 4;  // row tiles per group in the ragged-M tile order
+constexpr int kGroupM = kGemmGroupM;  // row tiles per group in the ragged-M tile order
 // k per LDS stage and ring slots: 64-deep stages make every k-contiguous tile
 // row one 128-byte line; two slots of a 256x256 tile fill 128 KB of LDS (a
 // 4-slot ring of 32-deep stages measured 5-10% slower on every product).

@@ -32,13 +32,16 @@ moe_status validate_shape(const moe_shape *s, std::string *why) {
   if (s->d > 65536 || s->F > 65536) return fail(why, MOE_ERR_UNSUPPORTED, "d or F > 65536");
   const int64_t R = s->T * (int64_t)s->k;
   if (s->T > ((int64_t)1 << 31) || R >= ((int64_t)1 << 31)) return fail(why, MOE_ERR_UNSUPPORTED, "T*k >= 2^31");
-  // every grid must fit in 2^31 - 8 workgroups
-  const int64_t lim = ((int64_t)1 << 31) - 8;
+  // every grid must fit in 2^31 - 1 workgroups; the bf16 bounds round like
+  // the launchers: ragged-M slots up to whole row-tile groups, grids up to a
+  // multiple of 8 (ragged M) or 64 (weight gradients)
+  const int64_t lim = ((int64_t)1 << 31) - 1;
   const int64_t wide = s->d > 2 * (int64_t)s->F ? s->d : 2 * (int64_t)s->F;
   int64_t gemm_blocks;
   if (s->dtype == MOE_DTYPE_BF16) {
-    gemm_blocks = (R / kGemmBM + s->E) * ceil_div(wide, kGemmBN / 2);
-    const int64_t wg = (int64_t)s->E * ceil_div(wide, kGemmBM) * ceil_div(wide, kGemmBN);
+    const int64_t slots = ceil_div(R / kGemmBM + s->E, kGemmGroupM) * kGemmGroupM;
+    gemm_blocks = ceil_div(slots * ceil_div(wide, kGemmBN / 2), 8) * 8;
+    const int64_t wg = ceil_div((int64_t)s->E * ceil_div(wide, kGemmBM) * ceil_div(wide, kGemmBN), 64) * 64;
     if (wg > gemm_blocks) gemm_blocks = wg;
   } else {
     gemm_blocks = (R / kGemmF32Tile + s->E) * ceil_div(wide, kGemmF32Tile);

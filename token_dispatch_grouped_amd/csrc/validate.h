@@ -16,6 +16,7 @@ constexpr int kRouteTokens = 256;       // tokens per top-k workgroup
 constexpr int kRouterChunksMax = 32;    // router weight-gradient partial sums
 constexpr int kGemmBM = 256;            // bf16 grouped GEMM rows per tile
 constexpr int kGemmBN = 256;            // bf16 grouped GEMM columns per tile
+constexpr int kGemmGroupM = 4;          // row tiles per group in the ragged-M tile order
 constexpr int kGemmF32Tile = 16;        // fp32 grouped GEMM tile edge
 constexpr int kAuxMaxBlocks = 1024;     // partial rows of the auxiliary-loss pass
 
