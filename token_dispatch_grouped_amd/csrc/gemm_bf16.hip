@@ -437,22 +437,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
-  const int bid = RAGGED_K ? xcd_run_remap(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
-  if (bid >= p.total) return;
-
   int e, m0, n_tile, m_valid, kdim;
   int64_t crow0;
   const bf16_t *Ab;
   const bf16_t *Bb;
   if (!RAGGED_K) {
     // logical order: groups of kGroupM row tiles, column tile outer inside a
-    // group, so the workgroups resident on one XCD share both operands
+    // group, so the workgroups resident on one XCD share both operands. The
+    // grid is sized for the most row tiles any routing can give; only the
+    // groups that hold real tiles are split over the XCDs.
+    MTileScan<BM> sc;
+    sc.run(p.offsets, p.E);
     const int per = kGroupM * p.n_tiles;
+    const int bid = xcd_share(blockIdx.x, min((sc.total + kGroupM - 1) / kGroupM * per, p.total));
+    if (bid < 0) return;
     const int grp = bid / per, rem = bid - grp * per;
     n_tile = rem / kGroupM;
     const int mslot = grp * kGroupM + (rem - n_tile * kGroupM);
     int mt;
-    if (!find_m_tile<BM>(p.offsets, p.E, mslot, e, mt)) return;
+    if (!sc.find(mslot, e, mt)) return;
     const int row0 = p.offsets[e];
     m0 = mt * BM;
     m_valid = min(BM, p.offsets[e + 1] - row0 - m0);
@@ -461,6 +464,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     Bb = p.B + (int64_t)e * p.strideB;
     kdim = p.K;
   } else {
+    const int bid = xcd_run_remap(blockIdx.x);
+    if (bid >= p.total) return;
     const int per_e = p.m_tiles * p.n_tiles;
     const int slot = bid / per_e;
     e = p.order ? p.order[slot] : slot;

@@ -5,9 +5,18 @@
 
 namespace moe {
 
-// Spread logical workgroups so that consecutive ones (which share their A
-// rows) run on the same XCD: hardware hands workgroup b to XCD b % 8.
-MOE_DEVICE int xcd_remap(int bid, int grid) { return (bid & 7) * (grid >> 3) + (bid >> 3); }
+// Hardware hands workgroup b to XCD b % 8, as the (b >> 3)-th of that XCD.
+// Give XCD x the contiguous logical range [x*L/8, (x+1)*L/8) of the L
+// logical workgroups that carry work, so that consecutive ones (which share
+// operands) run on one XCD and every XCD gets the same amount of work even
+// when the launch is an upper bound of L. Returns -1 past the XCD's share;
+// needs gridDim.x >= 8 * ceil(L/8).
+MOE_DEVICE int xcd_share(int b, int L) {
+  const int64_t x = b & 7;
+  const int64_t lo = (x * L) >> 3, hi = ((x + 1) * L) >> 3;
+  const int64_t bid = lo + (b >> 3);
+  return bid < hi ? (int)bid : -1;
+}
 
 // Balanced variant for work of uneven cost ordered heaviest first: runs of 8
 // consecutive logical workgroups (tiles that share an operand slab) stay on
@@ -18,43 +27,60 @@ MOE_DEVICE int xcd_run_remap(int bid) {
   return ((((q >> 3) << 3) + xcd) << 3) + (q & 7);
 }
 
-// Ragged-M tile lookup: the mslot-th BM-row tile over all experts in order.
-// Each lane sums the tiles of four experts, a wavefront scan finds the owner.
-// Returns false when mslot is past the last tile.
+// Ragged-M tiles: BM-row tiles over all experts in expert order. Each lane
+// counts the tiles of four experts (E <= 256) and a wavefront scan gives
+// every lane the tiles before its experts and the total.
 template <int BM>
-MOE_DEVICE bool find_m_tile(const int32_t *__restrict__ offsets, int E, int mslot, int &e_out, int &mt_out) {
-  const int lane = threadIdx.x & 63;
+struct MTileScan {
   int cnt[4];
-  int sum = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane * 4 + q;
-    int c = 0;
-    if (e < E) c = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-    cnt[q] = c;
-    sum += c;
-  }
-  const int inc = wave_inclusive_scan(sum);
-  const int exc = inc - sum;
-  const bool mine = mslot >= exc && mslot < inc;
-  const uint64_t bal = __ballot(mine);
-  if (bal == 0ull) return false;
-  const int src = __ffsll((unsigned long long)bal) - 1;
-  int e = 0, mt = 0;
-  if (mine) {
-    int r = mslot - exc;
+  int exc, inc;
+  int total;  // row tiles over all experts (wave-uniform)
+
+  MOE_DEVICE void run(const int32_t *__restrict__ offsets, int E) {
+    const int lane = threadIdx.x & 63;
+    int sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (r >= 0 && r < cnt[q]) {
-        e = lane * 4 + q;
-        mt = r;
-      }
-      r -= cnt[q];
+      const int e = lane * 4 + q;
+      int c = 0;
+      if (e < E) c = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      cnt[q] = c;
+      sum += c;
     }
+    inc = wave_inclusive_scan(sum);
+    exc = inc - sum;
+    total = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
   }
-  e_out = __shfl(e, src, 64);
-  mt_out = __shfl(mt, src, 64);
-  return true;
+  // Expert and tile within it of the mslot-th tile; false past the last.
+  MOE_DEVICE bool find(int mslot, int &e_out, int &mt_out) const {
+    const int lane = threadIdx.x & 63;
+    const bool mine = mslot >= exc && mslot < inc;
+    const uint64_t bal = __ballot(mine);
+    if (bal == 0ull) return false;
+    const int src = __ffsll((unsigned long long)bal) - 1;
+    int e = 0, mt = 0;
+    if (mine) {
+      int r = mslot - exc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (r >= 0 && r < cnt[q]) {
+          e = lane * 4 + q;
+          mt = r;
+        }
+        r -= cnt[q];
+      }
+    }
+    e_out = __shfl(e, src, 64);
+    mt_out = __shfl(mt, src, 64);
+    return true;
+  }
+};
+
+template <int BM>
+MOE_DEVICE bool find_m_tile(const int32_t *__restrict__ offsets, int E, int mslot, int &e_out, int &mt_out) {
+  MTileScan<BM> sc;
+  sc.run(offsets, E);
+  return sc.find(mslot, e_out, mt_out);
 }
 
 }  // namespace moe
