@@ -99,7 +99,8 @@ MOE_DEVICE int wave_inclusive_scan(int v) {
   return v;
 }
 
-MOE_DEVICE float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-MOE_DEVICE float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware reciprocal (about 1 ulp); e^-z = inf gives 0.
+MOE_DEVICE float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+MOE_DEVICE float silu_f(float z) { return z * sigmoid_f(z); }
 
 }  // namespace moe

@@ -213,52 +213,86 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
     __syncthreads();
     flush(BN / 2, p.C2, p.F, [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
   } else {  // EPI_SWIGLU_BWD: dA -> dH = (dH_gate | dH_up) using the saved h
-    // The tile is finished in WAVES_M row bands (one band per wavefront row
-    // wm). For each band the h_gate and h_up tiles arrive by LDS DMA into two
-    // [WM][BN] staging tiles; the band's wavefronts rewrite them in place as
-    // dH_gate and dH_up; all threads then store both.
-    // DMA layout: wave instruction q fills 1 KB = 1024/(2*BN) staged rows;
-    // lane l takes physical chunk l % (BN/8) of its row, i.e. logical chunk
-    // phys ^ (row & 15). Rows past m_valid and columns past N are clamped
-    // (their results are never stored). Every h element a workgroup reads
-    // lies in its own output tile and is read before the band holding it is
-    // stored, so dH may overwrite h in place (p.C == p.H).
-    static_assert(2 * WM * BN * 2 <= 160 * 1024, "two staged bands must fit in LDS");
-    const int n0 = n_tile * BN;
+    // The tile is finished in bands through two LDS buffers, each holding a
+    // band's h_gate and h_up tiles ([BR][BN] apiece, chunks swizzled as in
+    // the staging layout). Band b is accumulator row block i = b of every
+    // wavefront row: staged row r is tile row (r / 32) * WM + 32 b + r % 32,
+    // so all wavefronts share the arithmetic of every band. The first half
+    // of the wavefronts only loads (h by LDS DMA, so their vmcnt counts loads
+    // alone and waits in issue order), the second half only stores dH: the h
+    // of band b+1 is in flight while band b is rewritten in place as dH and
+    // then stored.
+    // DMA layout: wave instruction q fills 1 KB = RPI staged rows; lane l
+    // takes physical chunk l % CPR of its row, i.e. logical chunk
+    // phys ^ (row & 15). Rows past m_valid and columns past N are clamped;
+    // their results are never stored. Every valid h element a workgroup
+    // reads lies in its own output tile and is read before the band holding
+    // it is stored, so dH may overwrite h in place (p.C == p.H); a clamped
+    // row may read an already rewritten row, for a result that is dropped.
+    constexpr int BR = WAVES_M * 32;            // rows per band
+    constexpr int NBAND = FM;
+    constexpr int HALF = BR * BN;               // elements of one staged half
+    constexpr int BUF = 2 * HALF * 2;           // bytes of one buffer (gate + up)
     constexpr int CPR = BN / 8;
     constexpr int RPI = 1024 / (BN * 2);
-    constexpr int NI = WM * BN * 2 / (NT * 16);
-    static_assert(NI * NT * 16 == WM * BN * 2 && CPR >= 16, "h band/thread mismatch");
+    constexpr int NLW = NT / 128;               // loading wavefronts
+    constexpr int NI = BR / (RPI * NLW);        // DMA instructions per loader per half
+    constexpr int SCH = 2 * BR * CPR / (NT / 2);  // 16-byte chunks per storing thread
+    constexpr int SB = 8;                       // chunks read from LDS before storing
+    static_assert(2 * BUF <= 160 * 1024, "two band buffers must fit in LDS");
+    static_assert(NBAND * BR == BM && NI * RPI * NLW == BR && CPR >= 16, "band shape");
+    static_assert(SCH * (NT / 2) == 2 * BR * CPR && SCH % SB == 0 && (NT / 2) % CPR == 0, "store split");
+    const int n0 = n_tile * BN;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wv < NLW;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    bf16_t *sg_tile = stg;                 // [WM][BN] h_gate -> dH_gate
-    bf16_t *su_tile = stg + WM * BN;       // [WM][BN] h_up   -> dH_up
-    for (int band = 0; band < WAVES_M; ++band) {
-      const int rbase = band * WM;
-      if (rbase >= m_valid) break;  // uniform: the rest of the tile is past the expert's rows
+    auto tile_row = [](int b, int r) { return (r >> 5) * WM + b * 32 + (r & 31); };
+    // Each band takes an opaque copy of the lane index where it is used, so
+    // that no band's addressing is computed early (above the main loop or
+    // for all bands at once) and held in registers beside the accumulators.
+    auto issue_band = [&](int b) {
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
+      const uint32_t base = lds0 + (uint32_t)((b & 1) * BUF);
 #pragma unroll
       for (int q = 0; q < NI; ++q) {
-        const int r = (q * (NT / 64) + wv) * RPI + lane / CPR;
-        const int ch = (lane % CPR) ^ (r & 15);
+        const int r = (q * NLW + wv) * RPI + lane_e / CPR;
+        const int ch = (lane_e % CPR) ^ (r & 15);
         int gcol = n0 + ch * 8;
         if (gcol > p.N - 8) gcol = p.N - 8;
-        int rr = rbase + r;
+        int rr = tile_row(b, r);
         if (rr >= m_valid) rr = m_valid - 1;
         const bf16_t *src = p.H + (crow0 + rr) * p.ldc + gcol;
-        const uint32_t off = (uint32_t)((q * (NT / 64) + wv) * 1024);
-        dma16(src, lds0 + off);
-        dma16(src + p.F, lds0 + (uint32_t)(WM * BN * 2) + off);
+        const uint32_t off = (uint32_t)((q * NLW + wv) * 1024);
+        dma16(src, base + off);
+        dma16(src + p.F, base + (uint32_t)(HALF * 2) + off);
       }
-      wait_vm<0>();
-      __syncthreads();
-      if (wm == band) {
+    };
+    if (loader) {
+      issue_band(0);
+      if (NBAND > 1 && 32 < m_valid) issue_band(1);
+    }
+    // band b holds a valid row iff its first row (tile row 32 b) is valid
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int b = 0; b < NBAND; ++b) {
+      if (b * 32 >= m_valid) break;  // uniform: the later bands hold no valid row
+      const bool next = b + 1 < NBAND && (b + 1) * 32 < m_valid;
+      if (loader) {
+        if (next) wait_vm<2 * NI>();  // band b landed, band b+1 may still fly
+        else wait_vm<0>();
+      }
+      __syncthreads();
+      bf16_t *sg_tile = stg + (b & 1) * (2 * HALF);  // h_gate -> dH_gate
+      bf16_t *su_tile = sg_tile + HALF;             // h_up   -> dH_up
+      {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (i != b) continue;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int r = i * 32 + l32;
+              const int r = wm * 32 + l32;
               const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
               uint2 *pg = reinterpret_cast<uint2 *>(sg_tile + stg_off(r, col, BN));
               uint2 *pu = reinterpret_cast<uint2 *>(su_tile + stg_off(r, col, BN));
@@ -283,20 +317,39 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
               *pg = og;
               *pu = ou;
             }
+        }
       }
       __syncthreads();
-      // store the band: gate half then up half, 16 bytes per lane
-      constexpr int BCH = WM * CPR;  // chunks per staged band tile
-      for (int c = tid; c < 2 * BCH; c += NT) {
-        const int up = c >= BCH;
-        const int cc = up ? c - BCH : c;
-        const int r = cc / CPR, ch = cc - r * CPR;
-        if (rbase + r >= m_valid || n0 + ch * 8 >= p.N) continue;
-        const bf16_t *t = up ? su_tile : sg_tile;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + r * BN + ((ch ^ (r & 15)) << 3));
-        st16((bf16_t *)p.C + (crow0 + rbase + r) * p.ldc + (up ? p.F : 0) + n0 + ch * 8, v);
+      if (!loader) {
+        // thread st stores chunk st % CPR of rows st / CPR + k * (NT/2) / CPR,
+        // gate half first, SB chunks read from LDS before they are stored
+        int st = tid - NT / 2;
+        asm volatile("" : "+v"(st));
+        const int ch = st % CPR;
+        const bool col_ok = n0 + ch * 8 < p.N;
+#pragma unroll
+        for (int k0 = 0; k0 < SCH; k0 += SB) {
+          u32x4_t v[SB];
+#pragma unroll
+          for (int k = 0; k < SB; ++k) {
+            const int c = st + (k0 + k) * (NT / 2);
+            const int up = c >= BR * CPR;
+            const int r = (c - up * BR * CPR) / CPR;
+            v[k] = *reinterpret_cast<const u32x4_t *>(sg_tile + up * HALF + r * BN + ((ch ^ (r & 15)) << 3));
+          }
+#pragma unroll
+          for (int k = 0; k < SB; ++k) {
+            const int c = st + (k0 + k) * (NT / 2);
+            const int up = c >= BR * CPR;
+            const int r = (c - up * BR * CPR) / CPR;
+            const int tr = tile_row(b, r);
+            if (col_ok && tr < m_valid)
+              st16((bf16_t *)p.C + (crow0 + tr) * p.ldc + (up ? p.F : 0) + n0 + ch * 8, v[k]);
+          }
+        }
       }
-      __syncthreads();
+      __syncthreads();  // buffer b & 1 has been read out
+      if (loader && b + 2 < NBAND && (b + 2) * 32 < m_valid) issue_band(b + 2);
     }
   }
 }
