@@ -143,17 +143,31 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
     v.y = pack_bf2(x2, x3);
     *reinterpret_cast<uint2 *>(stg + stg_off(r, col, sw)) = v;
   };
-  // coalesced copy of a staged [BM][sw] tile to global memory; col_map gives
+  // coalesced copy of a staged [BM][SW] tile to global memory; col_map gives
   // the destination column of staged column c (a multiple of 8), or -1.
-  auto flush = [&](int sw, bf16_t *dst, int64_t ld, auto col_map) {
-    const int cpr = sw / 8;
-    for (int c = tid; c < BM * cpr; c += NT) {
-      const int r = c / cpr, ch = c - r * cpr;
-      if (r >= m_valid) continue;
-      const int gc = col_map(ch * 8);
-      if (gc < 0) continue;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + r * sw + ((ch ^ (r & 15)) << 3));
-      st16(dst + (crow0 + r) * ld + gc, v);
+  // Thread t copies chunk t % CPR of rows t / CPR + k * NT / CPR, reading
+  // SB chunks from LDS before storing them.
+  auto flush = [&](auto sw_c, bf16_t *dst, int64_t ld, auto col_map) {
+    constexpr int SW = decltype(sw_c)::value;
+    constexpr int CPR = SW / 8, RSTEP = NT / CPR, ITER = BM / RSTEP, SB = 4;
+    static_assert(NT % CPR == 0 && ITER * RSTEP == BM && ITER % SB == 0, "flush split");
+    int t = tid;
+    asm volatile("" : "+v"(t));  // addressing stays here, not above the main loop
+    const int ch = t % CPR, r0 = t / CPR;
+    const int gc = col_map(ch * 8);
+#pragma unroll
+    for (int k0 = 0; k0 < ITER; k0 += SB) {
+      u32x4_t v[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int r = r0 + (k0 + k) * RSTEP;
+        v[k] = *reinterpret_cast<const u32x4_t *>(stg + r * SW + ((ch ^ (r & 15)) << 3));
+      }
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int r = r0 + (k0 + k) * RSTEP;
+        if (r < m_valid && gc >= 0) st16(dst + (crow0 + r) * ld + gc, v[k]);
+      }
     }
   };
 
@@ -170,7 +184,7 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
         }
     __syncthreads();
     const int n0 = n_tile * BN;
-    flush(BN, (bf16_t *)p.C, p.ldc, [&](int c) { return n0 + c < p.N ? n0 + c : -1; });
+    flush(std::integral_constant<int, BN>{}, (bf16_t *)p.C, p.ldc, [&](int c) { return n0 + c < p.N ? n0 + c : -1; });
   } else if (EPI == EPI_SWIGLU_FWD) {
     // staged h tile: gate columns [0, BN/2), up columns [BN/2, BN)
     const int g0 = n_tile * (BN / 2);
@@ -189,7 +203,7 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
         }
     __syncthreads();
     if (p.C) {  // NULL when h is not kept (the activations are recomputed later)
-      flush(BN, (bf16_t *)p.C, p.ldc, [&](int c) {
+      flush(std::integral_constant<int, BN>{}, (bf16_t *)p.C, p.ldc, [&](int c) {
         if (c < BN / 2) return g0 + c < p.N ? g0 + c : -1;
         const int g = g0 + c - BN / 2;
         return g < p.N ? p.F + g : -1;
@@ -211,7 +225,7 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
                    silu_f(ga[4 * g + 2]) * ua[4 * g + 2], silu_f(ga[4 * g + 3]) * ua[4 * g + 3]);
         }
     __syncthreads();
-    flush(BN / 2, p.C2, p.F, [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
+    flush(std::integral_constant<int, BN / 2>{}, p.C2, p.F, [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
   } else {  // EPI_SWIGLU_BWD: dA -> dH = (dH_gate | dH_up) using the saved h
     // The tile is finished in bands through two LDS buffers, each holding a
     // band's h_gate and h_up tiles ([BR][BN] apiece, chunks swizzled as in
