@@ -531,9 +531,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     Bb = p.B + (int64_t)e * p.strideB;
     kdim = p.K;
   } else {
-    const int bid = xcd_run_remap(blockIdx.x);
-    if (bid >= p.total) return;
+    // experts come heaviest first and the empty ones last, so the tiles of
+    // the non-empty experts are the first ones of the logical order
     const int per_e = p.m_tiles * p.n_tiles;
+    const int bid = xcd_snake_runs(blockIdx.x, min(nonempty_experts(p.offsets, p.E) * per_e, p.total));
+    if (bid < 0) return;
     const int slot = bid / per_e;
     e = p.order ? p.order[slot] : slot;
     const int r = bid - slot * per_e;

@@ -20,11 +20,28 @@ MOE_DEVICE int xcd_share(int b, int L) {
 
 // Balanced variant for work of uneven cost ordered heaviest first: runs of 8
 // consecutive logical workgroups (tiles that share an operand slab) stay on
-// one XCD, and successive runs go to successive XCDs, so every XCD receives
-// its share of the heavy front of the order. The grid is a multiple of 64.
-MOE_DEVICE int xcd_run_remap(int bid) {
-  const int xcd = bid & 7, q = bid >> 3;
-  return ((((q >> 3) << 3) + xcd) << 3) + (q & 7);
+// one XCD, and the runs are dealt to the XCDs in snake order (0..7, 7..0,
+// 0..7, ...) over the L logical workgroups that carry work, so that every
+// XCD receives an even share of the heavy front of the order. Returns -1
+// past the end; needs gridDim.x >= 64 * ceil(L/64).
+MOE_DEVICE int xcd_snake_runs(int b, int L) {
+  const int x = b & 7, j = b >> 3;
+  const int rnd = j >> 3;
+  const int run = rnd * 8 + ((rnd & 1) ? 7 - x : x);
+  const int bid = run * 8 + (j & 7);
+  return bid < L ? bid : -1;
+}
+
+// Number of experts with at least one row (E <= 256), wave-uniform.
+MOE_DEVICE int nonempty_experts(const int32_t *__restrict__ offsets, int E) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    n += __popcll(__ballot(e < E && offsets[e + 1] > offsets[e]));
+  }
+  return __builtin_amdgcn_readfirstlane(n);
 }
 
 // Ragged-M tiles: BM-row tiles over all experts in expert order. Each lane
