@@ -522,10 +522,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     n_tile = rem / kGroupM;
     const int mslot = grp * kGroupM + (rem - n_tile * kGroupM);
     int mt;
-    if (!sc.find(mslot, e, mt)) return;
-    const int row0 = p.offsets[e];
+    int row0, row1;
+    if (!sc.find(mslot, e, mt, row0, row1)) return;
     m0 = mt * BM;
-    m_valid = min(BM, p.offsets[e + 1] - row0 - m0);
+    m_valid = min(BM, row1 - row0 - m0);
     crow0 = (int64_t)row0 + m0;
     Ab = p.A + crow0 * p.lda;
     Bb = p.B + (int64_t)e * p.strideB;

@@ -50,17 +50,22 @@ MOE_DEVICE int nonempty_experts(const int32_t *__restrict__ offsets, int E) {
 template <int BM>
 struct MTileScan {
   int cnt[4];
+  int first[5];  // offsets of the lane's four experts and the one after
   int exc, inc;
   int total;  // row tiles over all experts (wave-uniform)
 
   MOE_DEVICE void run(const int32_t *__restrict__ offsets, int E) {
     const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q <= 4; ++q) {
+      const int e = lane * 4 + q;
+      first[q] = e <= E ? offsets[e] : 0;
+    }
     int sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      int c = 0;
-      if (e < E) c = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      const int c = e < E ? (first[q + 1] - first[q] + BM - 1) / BM : 0;
       cnt[q] = c;
       sum += c;
     }
@@ -68,14 +73,15 @@ struct MTileScan {
     exc = inc - sum;
     total = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
   }
-  // Expert and tile within it of the mslot-th tile; false past the last.
-  MOE_DEVICE bool find(int mslot, int &e_out, int &mt_out) const {
+  // Expert, tile within it and the expert's row range [row0, row1) of the
+  // mslot-th tile; false past the last.
+  MOE_DEVICE bool find(int mslot, int &e_out, int &mt_out, int &row0_out, int &row1_out) const {
     const int lane = threadIdx.x & 63;
     const bool mine = mslot >= exc && mslot < inc;
     const uint64_t bal = __ballot(mine);
     if (bal == 0ull) return false;
     const int src = __ffsll((unsigned long long)bal) - 1;
-    int e = 0, mt = 0;
+    int e = 0, mt = 0, r0 = 0, r1 = 0;
     if (mine) {
       int r = mslot - exc;
 #pragma unroll
@@ -83,12 +89,16 @@ struct MTileScan {
         if (r >= 0 && r < cnt[q]) {
           e = lane * 4 + q;
           mt = r;
+          r0 = first[q];
+          r1 = first[q + 1];
         }
         r -= cnt[q];
       }
     }
     e_out = __shfl(e, src, 64);
     mt_out = __shfl(mt, src, 64);
+    row0_out = __shfl(r0, src, 64);
+    row1_out = __shfl(r1, src, 64);
     return true;
   }
 };
@@ -97,7 +107,8 @@ template <int BM>
 MOE_DEVICE bool find_m_tile(const int32_t *__restrict__ offsets, int E, int mslot, int &e_out, int &mt_out) {
   MTileScan<BM> sc;
   sc.run(offsets, E);
-  return sc.find(mslot, e_out, mt_out);
+  int r0, r1;
+  return sc.find(mslot, e_out, mt_out, r0, r1);
 }
 
 }  // namespace moe
