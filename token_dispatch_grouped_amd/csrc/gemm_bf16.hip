@@ -34,6 +34,8 @@
 // backward reads its h tile into LDS with coalesced loads and rewrites it in
 // place as dH. Weight gradients are read-modify-written in fp32, each element
 // by exactly one workgroup (no atomics), heaviest experts first.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -475,12 +477,10 @@ struct Operand {
   }
 };
 
-// Grouped GEMM with DMA-fed LDS stages: 2 slots of 64-deep k, the next
-// stage in flight while the current one is consumed. A and B are each either
-// k-contiguous or k-major (transposed in the fragment reads). Ragged M
-// (forward, dgrad) or ragged K (wgrad) over experts.
+// One output tile: operand set-up, the DMA-fed main loop and the epilogue.
 template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES>
-__global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
+MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_tile, int m_valid, int kdim,
+                        int64_t crow0, const bf16_t *Ab, const bf16_t *Bb) {
   constexpr int NT = NW * 64;
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
@@ -496,60 +496,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   constexpr int STG_BYTES = !SWAP ? 0 : BM * BN * 2;
   constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
-  __shared__ u32x4_t lds[LDS_BYTES / 16];
-
-  const int tid = threadIdx.x;
+  // opaque copy: nothing derived from the thread index is hoisted out of a
+  // persistent tile loop and held in registers across its tiles
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
-  int e, m0, n_tile, m_valid, kdim;
-  int64_t crow0;
-  const bf16_t *Ab;
-  const bf16_t *Bb;
-  if (!RAGGED_K) {
-    // logical order: groups of kGroupM row tiles, column tile outer inside a
-    // group, so the workgroups resident on one XCD share both operands. The
-    // grid is sized for the most row tiles any routing can give; only the
-    // groups that hold real tiles are split over the XCDs.
-    MTileScan<BM> sc;
-    sc.run(p.offsets, p.E);
-    const int per = kGroupM * p.n_tiles;
-    const int bid = xcd_share(blockIdx.x, min((sc.total + kGroupM - 1) / kGroupM * per, p.total));
-    if (bid < 0) return;
-    const int grp = bid / per, rem = bid - grp * per;
-    n_tile = rem / kGroupM;
-    const int mslot = grp * kGroupM + (rem - n_tile * kGroupM);
-    int mt;
-    int row0, row1;
-    if (!sc.find(mslot, e, mt, row0, row1)) return;
-    m0 = mt * BM;
-    m_valid = min(BM, row1 - row0 - m0);
-    crow0 = (int64_t)row0 + m0;
-    Ab = p.A + crow0 * p.lda;
-    Bb = p.B + (int64_t)e * p.strideB;
-    kdim = p.K;
-  } else {
-    // experts come heaviest first and the empty ones last, so the tiles of
-    // the non-empty experts are the first ones of the logical order
-    const int per_e = p.m_tiles * p.n_tiles;
-    const int bid = xcd_snake_runs(blockIdx.x, min(nonempty_experts(p.offsets, p.E) * per_e, p.total));
-    if (bid < 0) return;
-    const int slot = bid / per_e;
-    e = p.order ? p.order[slot] : slot;
-    const int r = bid - slot * per_e;
-    const int mt = r / p.n_tiles;
-    n_tile = r - mt * p.n_tiles;
-    const int row0 = p.offsets[e];
-    kdim = p.offsets[e + 1] - row0;
-    if (kdim <= 0) return;  // empty expert: dW stays bit-identical
-    m0 = mt * BM;
-    m_valid = min(BM, p.M - m0);
-    crow0 = 0;
-    Ab = p.A + (int64_t)row0 * p.lda + m0;      // k-major: column m0 at k = 0
-    Bb = p.B + (int64_t)row0 * p.ldb;
-  }
   const int n0 = n_tile * BN;
 
   OpA opa;
@@ -677,6 +632,83 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   epilogue<BM, BN, WM, WN, EPI, NT>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
 }
 
+// Grouped GEMM with DMA-fed LDS stages: 2 slots of 64-deep k, the next
+// stage in flight while the current one is consumed. A and B are each either
+// k-contiguous or k-major (transposed in the fragment reads). Ragged M
+// (forward, dgrad) or ragged K (wgrad) over experts.
+template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES>
+__global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int WAVES_N = BN / WN;
+  constexpr int WAVES_M = BM / WM;
+  static_assert(WAVES_M * WAVES_N == NW, "wavefront grid must cover the tile");
+  constexpr int FM = WM / 32, FN = WN / 32;
+  static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
+  static_assert(RAGGED_K == (EPI == EPI_ACC_F32), "weight gradients are the ragged-K products");
+  constexpr bool SWAP = EPI != EPI_ACC_F32;
+  using OpA = Operand<BM, AKM, NW, BK>;
+  using OpB = Operand<BN, BKM, NW, BK>;
+  constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
+  constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  constexpr int STG_BYTES = !SWAP ? 0 : BM * BN * 2;
+  constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+  __shared__ u32x4_t lds[LDS_BYTES / 16];
+  if (!RAGGED_K) {
+    // Persistent: the grid holds one workgroup per CU, 8-aligned, and XCD x
+    // works through its contiguous share of the logical order (see xcd_share)
+    // round-robin over its nW workgroups, so the tiles in flight on an XCD
+    // are consecutive ones. Logical order: groups of kGroupM row tiles,
+    // column tile outer inside a group, so the workgroups resident on one
+    // XCD share both operands; only the groups that hold real tiles count.
+    MTileScan<BM> sc;
+    sc.run(p.offsets, p.E);
+    const int per = kGroupM * p.n_tiles;
+    const int64_t L = min((sc.total + kGroupM - 1) / kGroupM * per, p.total);
+    const int64_t x = blockIdx.x & 7;
+    const int hi = (int)(((x + 1) * L) >> 3);
+    const int nW = gridDim.x >> 3;
+    for (int bid = (int)((x * L) >> 3) + (int)(blockIdx.x >> 3); bid < hi; bid += nW) {
+      const int grp = bid / per, rem = bid - grp * per;
+      const int n_tile = rem / kGroupM;
+      const int mslot = grp * kGroupM + (rem - n_tile * kGroupM);
+      int e, mt, row0, row1;
+      if (!sc.find(mslot, e, mt, row0, row1)) continue;  // row slot past the last tile
+      const int m0 = mt * BM;
+      const int64_t crow0 = (int64_t)row0 + m0;
+      gg_tile<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, BK, STAGES>(
+          p, lds, e, m0, n_tile, min(BM, row1 - row0 - m0), p.K, crow0, p.A + crow0 * p.lda,
+          p.B + (int64_t)e * p.strideB);
+      __syncthreads();  // the epilogue's LDS reads are done before the next tile's DMA
+    }
+  } else {
+    int e, m0, n_tile, m_valid, kdim;
+    int64_t crow0;
+    const bf16_t *Ab;
+    const bf16_t *Bb;
+    // experts come heaviest first and the empty ones last, so the tiles of
+    // the non-empty experts are the first ones of the logical order
+    const int per_e = p.m_tiles * p.n_tiles;
+    const int bid = xcd_snake_runs(blockIdx.x, min(nonempty_experts(p.offsets, p.E) * per_e, p.total));
+    if (bid < 0) return;
+    const int slot = bid / per_e;
+    e = p.order ? p.order[slot] : slot;
+    const int r = bid - slot * per_e;
+    const int mt = r / p.n_tiles;
+    n_tile = r - mt * p.n_tiles;
+    const int row0 = p.offsets[e];
+    kdim = p.offsets[e + 1] - row0;
+    if (kdim <= 0) return;  // empty expert: dW stays bit-identical
+    m0 = mt * BM;
+    m_valid = min(BM, p.M - m0);
+    crow0 = 0;
+    Ab = p.A + (int64_t)row0 * p.lda + m0;      // k-major: column m0 at k = 0
+    Bb = p.B + (int64_t)row0 * p.ldb;
+    gg_tile<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, BK, STAGES>(p, lds, e, m0, n_tile, m_valid, kdim, crow0,
+                                                                     Ab, Bb);
+  }
+}
+
 // Experts sorted by descending row count (ties by id), so that the longest
 // weight-gradient reductions start first. One workgroup, E <= 256.
 __global__ __launch_bounds__(256) void expert_order_kernel(const int32_t *__restrict__ offsets,
@@ -698,11 +730,25 @@ __global__ __launch_bounds__(256) void expert_order_kernel(const int32_t *__rest
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Workgroups of a persistent launch on the current device: one per CU, a
+// multiple of 8 so that every XCD holds the same number.
+static int persistent_grid() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 8;
+    cached[dev] = n / 8 * 8;
+  }
+  return cached[dev];
+}
+
 template <int BM, int BN, int WM, int WN, bool AKM, bool BKM, int EPI, bool RAGGED_K>
 static hipError_t run_dma(GemmParams p, hipStream_t s) {
   if (p.total <= 0) return hipSuccess;
   constexpr int NW = (BM / WM) * (BN / WN);
-  const int grid = RAGGED_K ? (p.total + 63) / 64 * 64 : (p.total + 7) / 8 * 8;
+  const int grid = RAGGED_K ? (p.total + 63) / 64 * 64 : std::min(persistent_grid(), (p.total + 7) / 8 * 8);
   gg_dma_kernel<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, kStageK, kStages>
       <<<dim3((unsigned)grid), NW * 64, 0, s>>>(p);
   return hipGetLastError();
