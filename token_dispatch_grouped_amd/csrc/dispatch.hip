@@ -118,12 +118,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ 
     const int c = lane + q * 64;
     if (c >= nc) break;
     float gv[V];
-    Elem<T>::unpack(ld16(dout + t * ld + (int64_t)c * V), gv);
+    Elem<T>::unpack(ld16_nt(dout + t * ld + (int64_t)c * V), gv);
     u32x4_t raw[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
-      raw[j] = ok ? ld16(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
+      raw[j] = ok ? ld16_nt(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
