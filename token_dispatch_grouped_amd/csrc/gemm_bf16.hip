@@ -85,9 +85,12 @@ MOE_DEVICE void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); 
 
 // Epilogue shared by the grouped GEMM kernels. With EPI_ACC_F32 the
 // accumulators are in MFMA order (lane = column); otherwise in swapped order
-// (lane = row, four consecutive columns per accumulator group) and `lds`
-// (at least BM*BN*2 bytes, or BM*BN*4 for EPI_SWIGLU_BWD) stages the tile.
-template <int BM, int BN, int WM, int WN, int EPI, int NT = 256>
+// (lane = row, four consecutive columns per accumulator group) and LDS stages
+// the tile. EPI_STORE stages one wavefront row (WM rows) at a time at byte
+// offset HALF_OFF, so that the LDS below HALF_OFF can already receive the
+// next tile's first stage; EPI_SWIGLU_FWD stages the whole tile (BM*BN*2
+// bytes) and EPI_SWIGLU_BWD two band buffers (2*BM*BN bytes) from offset 0.
+template <int BM, int BN, int WM, int WN, int EPI, int NT, int HALF_OFF>
 MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32], u32x4_t *lds, int e, int m0,
                          int n_tile, int m_valid, int64_t crow0, int wm, int wn) {
   constexpr int WAVES_M = BM / WM;
@@ -135,24 +138,25 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
   // LDS staging: rows of sw bf16 (sw/8 chunks), chunk c of row r stored at
   // chunk c ^ (r & 15).
   bf16_t *stg = reinterpret_cast<bf16_t *>(lds);
+  bf16_t *hstg = reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(lds) + HALF_OFF);
   auto stg_off = [](int r, int col, int sw) -> int {  // element offset, col % 4 == 0
     const int c = col >> 3;
     return r * sw + ((c ^ (r & 15)) << 3) + (col & 7);
   };
-  auto stg_put4 = [&](int r, int col, int sw, float x0, float x1, float x2, float x3) {
+  auto stg_put4 = [&](bf16_t *base, int r, int col, int sw, float x0, float x1, float x2, float x3) {
     uint2 v;
     v.x = pack_bf2(x0, x1);
     v.y = pack_bf2(x2, x3);
-    *reinterpret_cast<uint2 *>(stg + stg_off(r, col, sw)) = v;
+    *reinterpret_cast<uint2 *>(base + stg_off(r, col, sw)) = v;
   };
-  // coalesced copy of a staged [BM][SW] tile to global memory; col_map gives
-  // the destination column of staged column c (a multiple of 8), or -1.
-  // Thread t copies chunk t % CPR of rows t / CPR + k * NT / CPR, reading
-  // SB chunks from LDS before storing them.
-  auto flush = [&](auto sw_c, bf16_t *dst, int64_t ld, auto col_map) {
+  // coalesced copy of a staged [WM][SW] row band (tile rows row0 ..) to
+  // global memory; col_map gives the destination column of staged column c
+  // (a multiple of 8), or -1. Thread t copies chunk t % CPR of rows
+  // t / CPR + k * NT / CPR, reading SB chunks from LDS before storing them.
+  auto flush = [&](auto sw_c, const bf16_t *base, int row0, bf16_t *dst, int64_t ld, auto col_map) {
     constexpr int SW = decltype(sw_c)::value;
-    constexpr int CPR = SW / 8, RSTEP = NT / CPR, ITER = BM / RSTEP, SB = 4;
-    static_assert(NT % CPR == 0 && ITER * RSTEP == BM && ITER % SB == 0, "flush split");
+    constexpr int CPR = SW / 8, RSTEP = NT / CPR, ITER = WM / RSTEP, SB = ITER < 4 ? ITER : 4;
+    static_assert(NT % CPR == 0 && ITER * RSTEP == WM && ITER % SB == 0, "flush split");
     int t = tid;
     asm volatile("" : "+v"(t));  // addressing stays here, not above the main loop
     const int ch = t % CPR, r0 = t / CPR;
@@ -163,32 +167,40 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         const int r = r0 + (k0 + k) * RSTEP;
-        v[k] = *reinterpret_cast<const u32x4_t *>(stg + r * SW + ((ch ^ (r & 15)) << 3));
+        v[k] = *reinterpret_cast<const u32x4_t *>(base + r * SW + ((ch ^ (r & 15)) << 3));
       }
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         const int r = r0 + (k0 + k) * RSTEP;
-        if (r < m_valid && gc >= 0) st16(dst + (crow0 + r) * ld + gc, v[k]);
+        if (row0 + r < m_valid && gc >= 0) st16(dst + (crow0 + row0 + r) * ld + gc, v[k]);
       }
     }
   };
 
   if (EPI == EPI_STORE) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r = wm * WM + i * 32 + l32;
-          const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
-          stg_put4(r, col, BN, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        }
-    __syncthreads();
     const int n0 = n_tile * BN;
-    flush(std::integral_constant<int, BN>{}, (bf16_t *)p.C, p.ldc, [&](int c) { return n0 + c < p.N ? n0 + c : -1; });
+#pragma unroll
+    for (int h = 0; h < WAVES_M; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int r = i * 32 + l32;
+              const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
+              stg_put4(hstg, r, col, BN, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                       acc[i][j][4 * g + 3]);
+            }
+      }
+      __syncthreads();
+      flush(std::integral_constant<int, BN>{}, hstg, h * WM, (bf16_t *)p.C, p.ldc,
+            [&](int c) { return n0 + c < p.N ? n0 + c : -1; });
+      __syncthreads();
+    }
   } else if (EPI == EPI_SWIGLU_FWD) {
-    // staged h tile: gate columns [0, BN/2), up columns [BN/2, BN)
+    // staged h tile from offset 0: gate columns [0, BN/2), up columns [BN/2, BN)
     const int g0 = n_tile * (BN / 2);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -200,16 +212,18 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
           const int col = wn * (WN / 2) + j * 32 + 8 * g + 4 * lhi;
           const f32x16_t &ga = acc[i][j];
           const f32x16_t &ua = acc[i][j + FN / 2];
-          stg_put4(r, col, BN, ga[4 * g], ga[4 * g + 1], ga[4 * g + 2], ga[4 * g + 3]);
-          stg_put4(r, BN / 2 + col, BN, ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
+          stg_put4(stg, r, col, BN, ga[4 * g], ga[4 * g + 1], ga[4 * g + 2], ga[4 * g + 3]);
+          stg_put4(stg, r, BN / 2 + col, BN, ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
         }
     __syncthreads();
     if (p.C) {  // NULL when h is not kept (the activations are recomputed later)
-      flush(std::integral_constant<int, BN>{}, (bf16_t *)p.C, p.ldc, [&](int c) {
-        if (c < BN / 2) return g0 + c < p.N ? g0 + c : -1;
-        const int g = g0 + c - BN / 2;
-        return g < p.N ? p.F + g : -1;
-      });
+#pragma unroll
+      for (int h = 0; h < WAVES_M; ++h)
+        flush(std::integral_constant<int, BN>{}, stg + h * WM * BN, h * WM, (bf16_t *)p.C, p.ldc, [&](int c) {
+          if (c < BN / 2) return g0 + c < p.N ? g0 + c : -1;
+          const int g = g0 + c - BN / 2;
+          return g < p.N ? p.F + g : -1;
+        });
     }
     __syncthreads();
     // staged a = silu(gate) * up tile, BN/2 columns
@@ -223,11 +237,14 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
           const int col = wn * (WN / 2) + j * 32 + 8 * g + 4 * lhi;
           const f32x16_t &ga = acc[i][j];
           const f32x16_t &ua = acc[i][j + FN / 2];
-          stg_put4(r, col, BN / 2, silu_f(ga[4 * g]) * ua[4 * g], silu_f(ga[4 * g + 1]) * ua[4 * g + 1],
+          stg_put4(stg, r, col, BN / 2, silu_f(ga[4 * g]) * ua[4 * g], silu_f(ga[4 * g + 1]) * ua[4 * g + 1],
                    silu_f(ga[4 * g + 2]) * ua[4 * g + 2], silu_f(ga[4 * g + 3]) * ua[4 * g + 3]);
         }
     __syncthreads();
-    flush(std::integral_constant<int, BN / 2>{}, p.C2, p.F, [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
+#pragma unroll
+    for (int h = 0; h < WAVES_M; ++h)
+      flush(std::integral_constant<int, BN / 2>{}, stg + h * WM * (BN / 2), h * WM, p.C2, p.F,
+            [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
   } else {  // EPI_SWIGLU_BWD: dA -> dH = (dH_gate | dH_up) using the saved h
     // The tile is finished in bands through two LDS buffers, each holding a
     // band's h_gate and h_up tiles ([BR][BN] apiece, chunks swizzled as in
@@ -477,10 +494,21 @@ struct Operand {
   }
 };
 
+// Operands of the ragged-M tile a persistent workgroup computes next.
+struct NextTile {
+  const bf16_t *Ab;
+  const bf16_t *Bb;
+  int n_tile, m_valid;
+  bool valid;
+};
+
 // One output tile: operand set-up, the DMA-fed main loop and the epilogue.
+// `pre`: stage 0 of this tile was issued by the previous tile. With a valid
+// `nx` and the plain store epilogue (which leaves ring slot 0 alone), stage 0
+// of the next tile is issued into slot 0 before this tile's epilogue runs.
 template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES>
 MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_tile, int m_valid, int kdim,
-                        int64_t crow0, const bf16_t *Ab, const bf16_t *Bb) {
+                        int64_t crow0, const bf16_t *Ab, const bf16_t *Bb, bool pre, const NextTile &nx) {
   constexpr int NT = NW * 64;
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
@@ -493,7 +521,9 @@ MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_
   using OpB = Operand<BN, BKM, NW, BK>;
   constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
   constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-  constexpr int STG_BYTES = !SWAP ? 0 : BM * BN * 2;
+  // staging: one wavefront row in ring slot 1 for EPI_STORE, the whole tile
+  // for EPI_SWIGLU_FWD and EPI_SWIGLU_BWD (two band buffers)
+  constexpr int STG_BYTES = EPI == EPI_STORE ? STAGE_BYTES + WM * BN * 2 : !SWAP ? 0 : BM * BN * 2;
   constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
   // opaque copy: nothing derived from the thread index is hoisted out of a
@@ -507,23 +537,27 @@ MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_
 
   const int n0 = n_tile * BN;
 
+  auto init_ops = [&](OpA &oa, OpB &ob, const bf16_t *A_, const bf16_t *B_, int mv, int nt) {
+    const int nb0 = nt * BN;
+    oa.init(A_, p.lda, mv, wave, lane, [&](int r) { return r < mv ? r : mv - 1; });
+    if (EPI == EPI_SWIGLU_FWD) {
+      // B rows of the tile interleave gate and up rows per wavefront column
+      ob.init(B_, p.ldb, p.N, wave, lane, [&](int r) {
+        const int wcol = r / WN, q = r % WN;
+        const int gi = nt * (BN / 2) + wcol * (WN / 2) + (q % (WN / 2));
+        const int gc = gi < p.N ? gi : p.N - 1;  // past-the-end columns are masked on output
+        return q < WN / 2 ? gc : p.F + gc;
+      });
+    } else if (!BKM) {
+      ob.init(B_ + (int64_t)nb0 * p.ldb, p.ldb, p.N - nb0, wave, lane,
+              [&](int r) { return r < p.N - nb0 ? r : p.N - nb0 - 1; });
+    } else {
+      ob.init(B_ + nb0, p.ldb, p.N - nb0, wave, lane, [&](int r) { return r; });
+    }
+  };
   OpA opa;
   OpB opb;
-  opa.init(Ab, p.lda, m_valid, wave, lane, [&](int r) { return r < m_valid ? r : m_valid - 1; });
-  if (EPI == EPI_SWIGLU_FWD) {
-    // B rows of the tile interleave gate and up rows per wavefront column
-    opb.init(Bb, p.ldb, p.N, wave, lane, [&](int r) {
-      const int wcol = r / WN, q = r % WN;
-      const int gi = n_tile * (BN / 2) + wcol * (WN / 2) + (q % (WN / 2));
-      const int gc = gi < p.N ? gi : p.N - 1;  // past-the-end columns are masked on output
-      return q < WN / 2 ? gc : p.F + gc;
-    });
-  } else if (!BKM) {
-    opb.init(Bb + (int64_t)n0 * p.ldb, p.ldb, p.N - n0, wave, lane,
-             [&](int r) { return r < p.N - n0 ? r : p.N - n0 - 1; });
-  } else {
-    opb.init(Bb + n0, p.ldb, p.N - n0, wave, lane, [&](int r) { return r; });
-  }
+  init_ops(opa, opb, Ab, Bb, m_valid, n_tile);
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -603,7 +637,7 @@ MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_
   };
 #pragma unroll
   for (int st = 0; st < STAGES; ++st)
-    if (st < nk) issue(st);
+    if (st < nk && !(pre && st == 0)) issue(st);
   wait_stages(min(nk, STAGES) - 1);
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, 0, nk == 1);
@@ -629,7 +663,16 @@ MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_
     interleave();
   }
   __syncthreads();  // every wave is done with the ring before it is reused
-  epilogue<BM, BN, WM, WN, EPI, NT>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
+  if (EPI == EPI_STORE) {
+    if (nx.valid) {  // same K; the epilogue below stays clear of slot 0
+      OpA na;
+      OpB nb;
+      init_ops(na, nb, nx.Ab, nx.Bb, nx.m_valid, nx.n_tile);
+      na.issue(0, p.lda, kdim, lds0, wave_u);
+      nb.issue(0, p.ldb, kdim, lds0 + OpA::BYTES, wave_u);
+    }
+  }
+  epilogue<BM, BN, WM, WN, EPI, NT, STAGE_BYTES>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
 }
 
 // Grouped GEMM with DMA-fed LDS stages: 2 slots of 64-deep k, the next
@@ -650,7 +693,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   using OpB = Operand<BN, BKM, NW, BK>;
   constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
   constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-  constexpr int STG_BYTES = !SWAP ? 0 : BM * BN * 2;
+  // staging: one wavefront row in ring slot 1 for EPI_STORE, the whole tile
+  // for EPI_SWIGLU_FWD and EPI_SWIGLU_BWD (two band buffers)
+  constexpr int STG_BYTES = EPI == EPI_STORE ? STAGE_BYTES + WM * BN * 2 : !SWAP ? 0 : BM * BN * 2;
   constexpr int LDS_BYTES = RING_BYTES > STG_BYTES ? RING_BYTES : STG_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
   __shared__ u32x4_t lds[LDS_BYTES / 16];
@@ -668,17 +713,35 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     const int64_t x = blockIdx.x & 7;
     const int hi = (int)(((x + 1) * L) >> 3);
     const int nW = gridDim.x >> 3;
-    for (int bid = (int)((x * L) >> 3) + (int)(blockIdx.x >> 3); bid < hi; bid += nW) {
+    // logical workgroup -> expert, tile rows and column tile; false past the last tile
+    auto decode = [&](int bid, int &e, int &m0, int64_t &crow0, int &n_tile, int &m_valid) {
       const int grp = bid / per, rem = bid - grp * per;
-      const int n_tile = rem / kGroupM;
+      n_tile = rem / kGroupM;
       const int mslot = grp * kGroupM + (rem - n_tile * kGroupM);
-      int e, mt, row0, row1;
-      if (!sc.find(mslot, e, mt, row0, row1)) continue;  // row slot past the last tile
-      const int m0 = mt * BM;
-      const int64_t crow0 = (int64_t)row0 + m0;
+      int mt, row0, row1;
+      if (!sc.find(mslot, e, mt, row0, row1)) return false;
+      m0 = mt * BM;
+      crow0 = (int64_t)row0 + m0;
+      m_valid = min(BM, row1 - row0 - m0);
+      return true;
+    };
+    bool pre = false;  // this tile's stage 0 is already in flight
+    for (int bid = (int)((x * L) >> 3) + (int)(blockIdx.x >> 3); bid < hi; bid += nW) {
+      int e, m0, n_tile, m_valid;
+      int64_t crow0;
+      if (!decode(bid, e, m0, crow0, n_tile, m_valid)) {
+        pre = false;
+        continue;
+      }
+      NextTile nx;
+      int ne, nm0;
+      int64_t ncrow0;
+      nx.valid = bid + nW < hi && decode(bid + nW, ne, nm0, ncrow0, nx.n_tile, nx.m_valid);
+      nx.Ab = p.A + (nx.valid ? ncrow0 : 0) * p.lda;
+      nx.Bb = p.B + (int64_t)(nx.valid ? ne : 0) * p.strideB;
       gg_tile<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, BK, STAGES>(
-          p, lds, e, m0, n_tile, min(BM, row1 - row0 - m0), p.K, crow0, p.A + crow0 * p.lda,
-          p.B + (int64_t)e * p.strideB);
+          p, lds, e, m0, n_tile, m_valid, p.K, crow0, p.A + crow0 * p.lda, p.B + (int64_t)e * p.strideB, pre, nx);
+      pre = nx.valid && EPI == EPI_STORE;
       __syncthreads();  // the epilogue's LDS reads are done before the next tile's DMA
     }
   } else {
@@ -704,8 +767,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     crow0 = 0;
     Ab = p.A + (int64_t)row0 * p.lda + m0;      // k-major: column m0 at k = 0
     Bb = p.B + (int64_t)row0 * p.ldb;
+    const NextTile none{p.A, p.B, 0, 0, false};
     gg_tile<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, BK, STAGES>(p, lds, e, m0, n_tile, m_valid, kdim, crow0,
-                                                                     Ab, Bb);
+                                                                     Ab, Bb, false, none);
   }
 }
 
