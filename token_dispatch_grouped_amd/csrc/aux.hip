@@ -8,10 +8,12 @@
 //   dlogits[t,i] = p_i (G_i - sum_e p_e G_e) + (2 beta / T) lse p_i,
 //   G_e = alpha E counts[e] / (T^2 k)     (d(alpha L_bal)/dp[t,e])
 // overwriting or adding to dlogits. Each workgroup covers a contiguous run
-// of tokens, its four wavefronts taking every fourth token; their sums are
-// combined in a fixed order into one partial row [E + 3] per workgroup.
-// Pass 2 (aux_finalize_kernel, one workgroup): partial rows summed in
-// workgroup order, count statistics, losses and the metrics array.
+// of tokens, its four wavefronts taking every fourth token (four of their
+// tokens in flight at a time); their sums are combined in a fixed order into
+// one partial row [E + 3] per workgroup.
+// Pass 2 (aux_finalize_kernel, one workgroup): partial rows summed in eight
+// interleaved chains combined in a fixed order, count statistics, losses and
+// the metrics array.
 // No atomics: results are the same run to run.
 #include <math.h>
 
@@ -49,46 +51,78 @@ __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float *_
     psum[q] = 0.f;
   }
   float ent = 0.f, zz = 0.f, mx = 0.f;
-  for (int64_t t = t0 + wv; t < t_end; t += kAuxThreads / kWave) {
-    const float *row = logits + t * E;
-    float l[kAuxPerLane];
-    float m = -INFINITY;
+  // The wavefront's tokens t0 + wv + 4 i are taken TB at a time: loads and
+  // reductions of the TB tokens are independent chains that overlap; the
+  // per-lane sums still take the tokens in order.
+  constexpr int TB = 4;
+  constexpr int WSTEP = kAuxThreads / kWave;
+  for (int64_t tb = t0 + wv; tb < t_end; tb += TB * WSTEP) {
+    float l[TB][kAuxPerLane], m[TB];
 #pragma unroll
-    for (int q = 0; q < kAuxPerLane; ++q) {
-      const int e = lane + kWave * q;
-      l[q] = e < E ? row[e] : -INFINITY;
-      m = fmaxf(m, l[q]);
-    }
-    m = wave_max(m);
-    float ex[kAuxPerLane], s = 0.f;
-#pragma unroll
-    for (int q = 0; q < kAuxPerLane; ++q) {
-      ex[q] = expf(l[q] - m);  // 0 for -inf and for lanes past E
-      s += ex[q];
-    }
-    s = wave_sum(s);
-    const float inv = 1.f / s;
-    const float lse = m + logf(s);
-    float p[kAuxPerLane], plogp = 0.f, pg = 0.f;
-#pragma unroll
-    for (int q = 0; q < kAuxPerLane; ++q) {
-      p[q] = ex[q] * inv;
-      if (p[q] > 0.f) plogp += p[q] * (l[q] - lse);
-      pg += p[q] * G[q];
-      psum[q] += p[q];
-    }
-    ent -= wave_sum(plogp);
-    zz += lse * lse;
-    mx += inv;  // the top probability is exp(m - lse) = 1 / s
-    if (dlogits) {
-      pg = wave_sum(pg);
-      float *drow = dlogits + t * E;
+    for (int u = 0; u < TB; ++u) {
+      const int64_t t = tb + u * WSTEP;
+      m[u] = -INFINITY;
 #pragma unroll
       for (int q = 0; q < kAuxPerLane; ++q) {
         const int e = lane + kWave * q;
-        if (e < E) {
-          const float v = p[q] * (G[q] - pg) + zscale * lse * p[q];
-          drow[e] = accumulate ? drow[e] + v : v;
+        l[u][q] = (t < t_end && e < E) ? logits[t * E + e] : -INFINITY;
+        m[u] = fmaxf(m[u], l[u][q]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) m[u] = wave_max(m[u]);
+    float ex[TB][kAuxPerLane], sm[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      sm[u] = 0.f;
+#pragma unroll
+      for (int q = 0; q < kAuxPerLane; ++q) {
+        ex[u][q] = expf(l[u][q] - m[u]);  // 0 for -inf and for lanes past E
+        sm[u] += ex[u][q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) sm[u] = wave_sum(sm[u]);
+    float p[TB][kAuxPerLane], plogp[TB], pg[TB], lse[TB], inv[TB], old[TB][kAuxPerLane];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int64_t t = tb + u * WSTEP;
+      inv[u] = 1.f / sm[u];
+      lse[u] = m[u] + logf(sm[u]);
+      plogp[u] = 0.f;
+      pg[u] = 0.f;
+#pragma unroll
+      for (int q = 0; q < kAuxPerLane; ++q) {
+        const int e = lane + kWave * q;
+        p[u][q] = ex[u][q] * inv[u];
+        if (p[u][q] > 0.f) plogp[u] += p[u][q] * (l[u][q] - lse[u]);
+        pg[u] += p[u][q] * G[q];
+        old[u][q] = (dlogits && accumulate && t < t_end && e < E) ? dlogits[t * E + e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      plogp[u] = wave_sum(plogp[u]);
+      if (dlogits) pg[u] = wave_sum(pg[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int64_t t = tb + u * WSTEP;
+      if (t >= t_end) break;  // uniform: the rest of the batch is past the run
+#pragma unroll
+      for (int q = 0; q < kAuxPerLane; ++q) psum[q] += p[u][q];
+      ent -= plogp[u];
+      zz += lse[u] * lse[u];
+      mx += inv[u];  // the top probability is exp(m - lse) = 1 / s
+      if (dlogits) {
+        float *drow = dlogits + t * E;
+#pragma unroll
+        for (int q = 0; q < kAuxPerLane; ++q) {
+          const int e = lane + kWave * q;
+          if (e < E) {
+            const float v = p[u][q] * (G[q] - pg[u]) + zscale * lse[u] * p[u][q];
+            drow[e] = accumulate ? old[u][q] + v : v;
+          }
         }
       }
     }
@@ -150,8 +184,14 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(const float *
   const float mean = (float)((double)T * k / E);
   float fP = 0.f, dev2 = 0.f, cmax = 0.f, empty = 0.f;
   if (e < E) {
-    float P = 0.f;
-    for (int b = 0; b < nblk; ++b) P += partial[(int64_t)b * ld + e];
+    // eight interleaved partial sums (rows b = r mod 8), added in a fixed order
+    float P8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) P8[r] += partial[(int64_t)(b + r) * ld + e];
+    for (int r = 0; b + r < nblk; ++r) P8[r] += partial[(int64_t)(b + r) * ld + e];
+    float P = ((P8[0] + P8[1]) + (P8[2] + P8[3])) + ((P8[4] + P8[5]) + (P8[6] + P8[7]));
     P /= Tf;
     const float c = (float)counts[e];
     const float f = c / rows;
@@ -165,8 +205,15 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(const float *
     }
   }
   float sc = 0.f;
-  if (e < kAuxScalars)
-    for (int b = 0; b < nblk; ++b) sc += partial[(int64_t)b * ld + E + e];
+  if (e < kAuxScalars) {
+    float S8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) S8[r] += partial[(int64_t)(b + r) * ld + E + e];
+    for (int r = 0; b + r < nblk; ++r) S8[r] += partial[(int64_t)(b + r) * ld + E + e];
+    sc = ((S8[0] + S8[1]) + (S8[2] + S8[3])) + ((S8[4] + S8[5]) + (S8[6] + S8[7]));
+  }
   const float sum_fP = block_sum_256(fP, red);
   const float sum_dev2 = block_sum_256(dev2, red);
   const float sum_empty = block_sum_256(empty, red);
