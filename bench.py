@@ -57,16 +57,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "5e239ba1b1924deb0f81328a722ef854b926bab4c750b7c762a3d73931f6aae4",
+    "sources_sha256": "1bf0ffa1aca26e46c28bf550214dd6a6943c2c091bc1b2a1417fb280c1d8044e",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.846 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.427 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.439 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.772 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (5.108 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.660 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.565 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.475 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.452 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.790 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.982 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.665 + 0.645) * 2 ** 30,
     },
 }
 

@@ -162,6 +162,9 @@ SMALL_CASES = [
     ("bf16_router_small", small_workload(512, 256, 8, 2, 256, BF16, "router", seed=26, n_empty=1), False),
     ("f32_zipf", small_workload(200, 128, 16, 4, 128, F32, "zipf", seed=27, n_empty=4), False),
     ("bf16_E256_k16", small_workload(130, 64, 256, 16, 64, BF16, "normal", seed=28), False),
+    # F = 64: the down forward is one 64-deep stage, and with d = 2048 its ~560 tiles give every persistent
+    # workgroup several, so a tile whose only stage was issued during the previous tile's epilogue runs
+    ("bf16_F64_multi_tile", small_workload(4096, 2048, 8, 4, 64, BF16, "zipf", seed=29, n_empty=1), False),
 ]
 
 

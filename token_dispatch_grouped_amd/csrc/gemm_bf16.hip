@@ -17,23 +17,30 @@
 // `offsets` on the device, so an expert with no rows gets no tile at all and
 // any M_e (0 included) needs no padding.
 //
-// Tiling: a 256-thread workgroup (4 wavefronts, 2x2) computes a BM x BN
-// tile; each wavefront owns a WM x WN sub-tile of v_mfma_f32_32x32x16_bf16
-// results held in fp32. k advances in steps of 64, double-buffered in LDS:
-// the next step's global loads are issued before the current step's MFMAs.
-// Both operands sit in LDS k-contiguous, in 16-byte chunks with an XOR
-// swizzle that keeps the fragment reads and the tile writes free of bank
-// conflicts. Transposed operands are made k-contiguous on the way in: each
-// thread loads an 8(k) x 8 block with eight 16-byte loads and transposes it
-// in registers.
+// Tiling: a 512-thread workgroup (8 wavefronts, 2 x 4) computes a 256 x 256
+// tile; each wavefront owns a 128 x 64 sub-tile of v_mfma_f32_32x32x16_bf16
+// results held in fp32. k advances 64 at a time through a 2-slot LDS ring
+// filled by the LDS DMA (global_load_lds_dwordx4, tile data never passes
+// through registers): the next stage is in flight while the current one is
+// consumed. k-contiguous operands sit in 128-byte LDS rows with an XOR chunk
+// swizzle; k-major operands are copied as they are and read through the
+// transposing ds_read_b64_tr_b16.
+//
+// Scheduling: the ragged-M products run persistent, one workgroup per CU,
+// each XCD walking a contiguous share of the tiles (groups of 4 row tiles x
+// all column tiles) round-robin; the weight gradients run one workgroup per
+// tile, experts heaviest first, runs of 8 tiles dealt to the XCDs in snake
+// order.
 //
 // Epilogues: bf16 outputs are staged through LDS and written with 16-byte,
 // fully coalesced stores (the MFMA is issued with its operands swapped so
-// that each lane holds four consecutive output columns). The SwiGLU forward
-// writes h and a = silu(gate) * up from the fp32 accumulators; the SwiGLU
-// backward reads its h tile into LDS with coalesced loads and rewrites it in
-// place as dH. Weight gradients are read-modify-written in fp32, each element
-// by exactly one workgroup (no atomics), heaviest experts first.
+// that each lane holds four consecutive output columns); the plain store
+// stages one wavefront row at a time so that the next tile's first stage can
+// land in the other ring slot meanwhile. The SwiGLU forward writes h and
+// a = silu(gate) * up from the fp32 accumulators; the SwiGLU backward loads
+// its h bands into LDS by DMA and rewrites them in place as dH. Weight
+// gradients are read-modify-written in fp32, each element by exactly one
+// workgroup (no atomics).
 #include <algorithm>
 
 #include "common.h"
@@ -701,7 +708,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   __shared__ u32x4_t lds[LDS_BYTES / 16];
   if (!RAGGED_K) {
     // Persistent: the grid holds one workgroup per CU, 8-aligned, and XCD x
-    // works through its contiguous share of the logical order (see xcd_share)
+    // works through its contiguous share of the logical order (xcd_range)
     // round-robin over its nW workgroups, so the tiles in flight on an XCD
     // are consecutive ones. Logical order: groups of kGroupM row tiles,
     // column tile outer inside a group, so the workgroups resident on one
@@ -710,8 +717,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     sc.run(p.offsets, p.E);
     const int per = kGroupM * p.n_tiles;
     const int64_t L = min((sc.total + kGroupM - 1) / kGroupM * per, p.total);
-    const int64_t x = blockIdx.x & 7;
-    const int hi = (int)(((x + 1) * L) >> 3);
+    int lo, hi;
+    xcd_range(blockIdx.x & 7, L, lo, hi);
     const int nW = gridDim.x >> 3;
     // logical workgroup -> expert, tile rows and column tile; false past the last tile
     auto decode = [&](int bid, int &e, int &m0, int64_t &crow0, int &n_tile, int &m_valid) {
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
       return true;
     };
     bool pre = false;  // this tile's stage 0 is already in flight
-    for (int bid = (int)((x * L) >> 3) + (int)(blockIdx.x >> 3); bid < hi; bid += nW) {
+    for (int bid = lo + (int)(blockIdx.x >> 3); bid < hi; bid += nW) {
       int e, m0, n_tile, m_valid;
       int64_t crow0;
       if (!decode(bid, e, m0, crow0, n_tile, m_valid)) {
@@ -826,8 +833,10 @@ static GemmParams base_params(const GroupedFfnArgs &a) {
   return p;
 }
 
-// Ragged-M grid: an upper bound of the number of BM-row tiles over all
-// experts (sum of ceil(M_e/BM) <= R/BM + E), times the column tiles.
+// Ragged-M logical tile count: an upper bound of the number of BM-row tiles
+// over all experts (sum of ceil(M_e/BM) <= R/BM + E, rounded up to whole
+// row-tile groups), times the column tiles. The persistent launch splits the
+// real tiles it finds on the device, never more than this.
 static int ragged_m_total(int64_t R, int E, int BM, int n_tiles) {
   const int64_t slots = (R / BM + E + kGroupM - 1) / kGroupM * kGroupM;
   return (int)(slots * (int64_t)n_tiles);

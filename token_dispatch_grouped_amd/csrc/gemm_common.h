@@ -5,17 +5,14 @@
 
 namespace moe {
 
-// Hardware hands workgroup b to XCD b % 8, as the (b >> 3)-th of that XCD.
-// Give XCD x the contiguous logical range [x*L/8, (x+1)*L/8) of the L
-// logical workgroups that carry work, so that consecutive ones (which share
-// operands) run on one XCD and every XCD gets the same amount of work even
-// when the launch is an upper bound of L. Returns -1 past the XCD's share;
-// needs gridDim.x >= 8 * ceil(L/8).
-MOE_DEVICE int xcd_share(int b, int L) {
-  const int64_t x = b & 7;
-  const int64_t lo = (x * L) >> 3, hi = ((x + 1) * L) >> 3;
-  const int64_t bid = lo + (b >> 3);
-  return bid < hi ? (int)bid : -1;
+// Hardware hands workgroup b to XCD b % 8. XCD x owns the contiguous logical
+// range [lo, hi) = [x*L/8, (x+1)*L/8) of the L logical workgroups that carry
+// work, so that consecutive ones (which share operands) run on one XCD and
+// every XCD gets the same amount of work even when the launch is sized for
+// more.
+MOE_DEVICE void xcd_range(int x, int64_t L, int &lo, int &hi) {
+  lo = (int)(((int64_t)x * L) >> 3);
+  hi = (int)(((int64_t)(x + 1) * L) >> 3);
 }
 
 // Balanced variant for work of uneven cost ordered heaviest first: runs of 8

@@ -32,9 +32,10 @@ moe_status validate_shape(const moe_shape *s, std::string *why) {
   if (s->d > 65536 || s->F > 65536) return fail(why, MOE_ERR_UNSUPPORTED, "d or F > 65536");
   const int64_t R = s->T * (int64_t)s->k;
   if (s->T > ((int64_t)1 << 31) || R >= ((int64_t)1 << 31)) return fail(why, MOE_ERR_UNSUPPORTED, "T*k >= 2^31");
-  // every grid must fit in 2^31 - 1 workgroups; the bf16 bounds round like
-  // the launchers: ragged-M slots up to whole row-tile groups, grids up to a
-  // multiple of 8 (ragged M) or 64 (weight gradients)
+  // every tile count must fit in 2^31 - 1; the bf16 bounds round like the
+  // launchers: ragged-M row slots up to whole row-tile groups and the logical
+  // tile count up to a multiple of 8, weight-gradient grids up to a multiple
+  // of 64
   const int64_t lim = ((int64_t)1 << 31) - 1;
   const int64_t wide = s->d > 2 * (int64_t)s->F ? s->d : 2 * (int64_t)s->F;
   int64_t gemm_blocks;
