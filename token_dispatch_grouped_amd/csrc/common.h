@@ -27,7 +27,12 @@ MOE_DEVICE bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); 
 
 // two fp32 -> packed bf16 pair (low half = a)
 MOE_DEVICE uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  // one two-lane conversion (v_cvt_pk_bf16_f32 with both sources), each
+  // element rounded to nearest even as f2bf does
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T> struct Elem;
