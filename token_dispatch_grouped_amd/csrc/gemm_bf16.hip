@@ -168,6 +168,9 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
     asm volatile("" : "+v"(t));  // addressing stays here, not above the main loop
     const int ch = t % CPR, r0 = t / CPR;
     const int gc = col_map(ch * 8);
+    // the thread's rows are RSTEP apart: one row pointer, stepped
+    bf16_t *rowp = dst + (crow0 + row0 + r0) * ld + (gc < 0 ? 0 : gc);
+    const int64_t step = (int64_t)RSTEP * ld;
 #pragma unroll
     for (int k0 = 0; k0 < ITER; k0 += SB) {
       u32x4_t v[SB];
@@ -179,7 +182,8 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         const int r = r0 + (k0 + k) * RSTEP;
-        if (row0 + r < m_valid && gc >= 0) st16(dst + (crow0 + row0 + r) * ld + gc, v[k]);
+        if (row0 + r < m_valid && gc >= 0) st16(rowp, v[k]);
+        rowp += step;
       }
     }
   };
