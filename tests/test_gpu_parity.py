@@ -168,6 +168,42 @@ SMALL_CASES = [
 ]
 
 
+def _random_cases(n=14, seed=2024):
+    """Seeded random layer shapes within the supported matrix (d, F multiples of 64, k <= E <= 256),
+    sized so the oracle finishes in a second or two: tile edges, ragged tails, empty experts and both
+    dtypes in combinations the hand-picked cases do not cover."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = BF16 if rng.random() < 0.75 else F32
+        E = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 31, 64, 100]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        d = 64 * int(rng.integers(1, 9))
+        F = 64 * int(rng.integers(1, 9))
+        T = int(rng.integers(1, 2049))
+        if 18.0 * T * k * d * F > 3e10:
+            continue
+        routing = "zipf" if rng.random() < 0.6 else "normal"
+        n_empty = int(rng.integers(0, E - k + 1)) if routing == "zipf" and E > k else 0
+        renorm = bool(rng.random() < 0.3)
+        s = int(rng.integers(100, 10_000))
+        name = f"rand{len(cases)}_T{T}_d{d}_E{E}_k{k}_F{F}_{dtype}_{routing}{n_empty}{'_renorm' if renorm else ''}"
+        cases.append((name, small_workload(T, d, E, k, F, dtype, routing, seed=s, n_empty=n_empty), renorm))
+    return cases
+
+
+RANDOM_CASES = _random_cases()
+
+
+@pytest.mark.parametrize("name,w,renorm", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_layer_random_shapes(name, w, renorm):
+    print(f"[parity] {name}", flush=True)
+    inp = make_inputs(w)
+    gres, gacc = gpu_run(w, inp, renorm)
+    ores, oacc = oracle_run(w, inp, renorm)
+    compare(w, gres, gacc, ores, oacc, renorm)
+
+
 @pytest.mark.parametrize("name,w,renorm", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
 def test_layer_small(name, w, renorm):
     print(f"[parity] {name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F} {w.dtype}", flush=True)
