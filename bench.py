@@ -57,16 +57,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "1bf0ffa1aca26e46c28bf550214dd6a6943c2c091bc1b2a1417fb280c1d8044e",
+    "sources_sha256": "fbd4f09872d32ed8583bd8386eb43a3c5a30733e0ef6ac7d86cdd306ca848b47",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.565 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.475 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.452 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.790 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (4.982 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.665 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.840 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.430 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.553 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.812 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.981 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.668 + 0.645) * 2 ** 30,
     },
 }
 
