@@ -348,10 +348,13 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
               float dg[4], du[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const float da = acc[i][j][4 * g + q];
+                // t = dA s, dH_up = t hg, dH_gate = t hu (1 + hg (1 - s)) = th + th u
+                // with th = t hu and u = hg - hg s (s = sigmoid(hg))
                 const float sgm = sigmoid_f(hg[q]);
-                dg[q] = da * hu[q] * sgm * (1.f + hg[q] * (1.f - sgm));
-                du[q] = da * hg[q] * sgm;
+                const float t = acc[i][j][4 * g + q] * sgm;
+                const float th = t * hu[q];
+                du[q] = t * hg[q];
+                dg[q] = fmaf(th, fmaf(-hg[q], sgm, hg[q]), th);
               }
               uint2 og, ou;
               og.x = pack_bf2(dg[0], dg[1]);
