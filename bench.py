@@ -57,16 +57,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "fbd4f09872d32ed8583bd8386eb43a3c5a30733e0ef6ac7d86cdd306ca848b47",
+    "sources_sha256": "7d0c857d6310c834a81f6fb81be97273b62a34517cb28961b2b9cb20626ee353",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.840 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.430 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.553 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.812 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (4.981 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.668 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.635 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.453 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.579 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.771 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.904 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.662 + 0.645) * 2 ** 30,
     },
 }
 
