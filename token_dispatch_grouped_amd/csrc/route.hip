@@ -67,6 +67,38 @@ MOE_DEVICE uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Visit row[0..E) in ascending order, f(e, value). With E % 4 == 0 (rows
+// then 16-byte aligned) the row is read 16 values at a time by four 16-byte
+// loads issued together, so that a thread waits for one round trip per 16
+// values instead of one per value.
+template <typename F>
+MOE_DEVICE void for_row(const float *__restrict__ row, int E, F f) {
+  int e0 = 0;
+  if ((E & 3) == 0) {
+    for (; e0 + 16 <= E; e0 += 16) {
+      float4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const float4 *>(row + e0 + 4 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f(e0 + 4 * i, v[i].x);
+        f(e0 + 4 * i + 1, v[i].y);
+        f(e0 + 4 * i + 2, v[i].z);
+        f(e0 + 4 * i + 3, v[i].w);
+      }
+    }
+    for (; e0 < E; e0 += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(row + e0);
+      f(e0, v.x);
+      f(e0 + 1, v.y);
+      f(e0 + 2, v.z);
+      f(e0 + 3, v.w);
+    }
+    return;
+  }
+  for (; e0 < E; ++e0) f(e0, row[e0]);
+}
+
 // ---------------------------------------------------------------------------
 // A2 + first half of A3: per token top-k and weights; per workgroup the
 // stable rank of each (token, slot) among the workgroup's slots of the same
@@ -74,10 +106,13 @@ MOE_DEVICE uint32_t order_key(float f) {
 //
 // One thread per token, 256 tokens per workgroup (4 wavefronts). Top-k keeps
 // a descending list of 64-bit composite keys (logit key, then inverted id so
-// that the lower id wins a tie). Ranks within a wavefront come from ballots
-// over the bits of the expert id (every lane learns, for its own expert,
-// which lanes hold the same expert in each slot column); ranks across
-// wavefronts from per-wavefront counts in LDS. No atomics decide any order.
+// that the lower id wins a tie). A token selects an expert at most once, so
+// the rank of slot (t, j) among the workgroup's slots of expert e is the
+// number of earlier tokens of the workgroup that selected e. Each wavefront
+// builds in LDS, per expert, the 64-bit mask of its lanes that selected it
+// (bitwise OR, whose result does not depend on the order of the updates);
+// the rank is the population count of the masks of earlier wavefronts plus
+// that of the own mask below the lane. No atomic decides any order.
 // ---------------------------------------------------------------------------
 template <int KMAX>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
@@ -85,15 +120,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
                                                          float *__restrict__ topk_w,
                                                          int32_t *__restrict__ local_rank,
                                                          int32_t *__restrict__ blk_cnt, int64_t ntok, int E,
-                                                         int k, int id_bits, int renorm) {
-  __shared__ int32_t s_wcnt[4][256];
+                                                         int k, int renorm) {
+  __shared__ unsigned long long s_mask[4][256];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int64_t t = (int64_t)blockIdx.x * 256 + tid;
   const bool valid = t < ntok;
 
-  for (int i = tid; i < 4 * 256; i += 256) (&s_wcnt[0][0])[i] = 0;
+  for (int i = tid; i < 4 * 256; i += 256) (&s_mask[0][0])[i] = 0ull;
 
   uint64_t list[KMAX];
 #pragma unroll
@@ -102,27 +137,25 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
   float w[KMAX];
   if (valid) {
     const float *row = logits + t * E;
-    for (int e = 0; e < E; ++e) {
-      uint64_t c = ((uint64_t)order_key(row[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+    for_row(row, E, [&](int e, float l) {
+      uint64_t c = ((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
       if (c > list[KMAX - 1]) {
+        // insert into the descending list: entries above c stay, c takes the
+        // first place it beats, the entries below shift down one place
+        bool g[KMAX];
 #pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-          uint64_t hi = c > list[i] ? c : list[i];
-          uint64_t lo = c > list[i] ? list[i] : c;
-          list[i] = hi;
-          c = lo;
-        }
+        for (int i = 0; i < KMAX; ++i) g[i] = c > list[i];
+#pragma unroll
+        for (int i = KMAX - 1; i > 0; --i) list[i] = g[i - 1] ? list[i - 1] : (g[i] ? c : list[i]);
+        list[0] = g[0] ? c : list[0];
       }
-    }
+    });
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) ids[i] = (int)(0xffffffffu - (uint32_t)(list[i] & 0xffffffffu));
     // softmax over the whole row; the first selected logit is the maximum
     const float m = row[ids[0]];
     float sum = 0.f;
-    for (int e = 0; e < E; ++e) {
-      float l = row[e];
-      sum += (l == l) ? expf(l - m) : 0.f;
-    }
+    for_row(row, E, [&](int, float l) { sum += (l == l) ? expf(l - m) : 0.f; });
     float wsum = 0.f;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
@@ -145,51 +178,27 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) ids[i] = 0;
   }
-  __syncthreads();  // s_wcnt cleared
-
-  // ranks within the wavefront
-  const uint64_t vmask = __ballot(valid);
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int below[KMAX], total[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) below[j] = total[j] = 0;
-#pragma unroll
-  for (int jc = 0; jc < KMAX; ++jc) {
-    if (jc >= k) break;
-    uint64_t bal[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) bal[b] = (b < id_bits) ? __ballot((ids[jc] >> b) & 1) : 0ull;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
-        uint64_t mm = vmask;
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-          if (b < id_bits) mm &= ((ids[j] >> b) & 1) ? bal[b] : ~bal[b];
-        below[j] += __popcll(mm & lt);
-        total[j] += __popcll(mm);
-      }
-    }
-  }
-  // the first lane of the wavefront holding expert e publishes the count
+  __syncthreads();  // masks cleared
   if (valid) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k && below[j] == 0) s_wcnt[wave][ids[j]] = total[j];
+      if (j < k) atomicOr(&s_mask[wave][ids[j]], 1ull << lane);
   }
   __syncthreads();
   if (valid) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j < k) {
-        int pre = 0;
-        for (int w2 = 0; w2 < wave; ++w2) pre += s_wcnt[w2][ids[j]];
-        local_rank[t * k + j] = pre + below[j];
+        int pre = __popcll(s_mask[wave][ids[j]] & below);
+        for (int w2 = 0; w2 < wave; ++w2) pre += __popcll(s_mask[w2][ids[j]]);
+        local_rank[t * k + j] = pre;
       }
     }
   }
   for (int e = tid; e < E; e += 256)
-    blk_cnt[(int64_t)blockIdx.x * E + e] = s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e];
+    blk_cnt[(int64_t)blockIdx.x * E + e] = __popcll(s_mask[0][e]) + __popcll(s_mask[1][e]) +
+                                           __popcll(s_mask[2][e]) + __popcll(s_mask[3][e]);
 }
 
 // Block-wide exclusive scan of one int per thread (256 threads); returns the
@@ -288,8 +297,12 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict_
     }
   }
   if (renorm) {
-    if (!accumulate)
-      for (int e = 0; e < E; ++e) drow[e] = 0.f;
+    if (!accumulate) {
+      if ((E & 3) == 0)
+        for (int e = 0; e < E; e += 4) *reinterpret_cast<float4 *>(drow + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+      else
+        for (int e = 0; e < E; ++e) drow[e] = 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (j < k) drow[ids[j]] = accumulate ? drow[ids[j]] + w[j] * (g[j] - s) : w[j] * (g[j] - s);
@@ -300,20 +313,26 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict_
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) base[j] = (accumulate && j < k) ? drow[ids[j]] : 0.f;
   float m = -INFINITY;
-  for (int e = 0; e < E; ++e) {
-    float l = row[e];
+  for_row(row, E, [&](int, float l) {
     if (l == l) m = fmaxf(m, l);
-  }
+  });
   float sum = 0.f;
-  for (int e = 0; e < E; ++e) {
-    float l = row[e];
-    sum += (l == l) ? expf(l - m) : 0.f;
-  }
+  for_row(row, E, [&](int, float l) { sum += (l == l) ? expf(l - m) : 0.f; });
   const float inv = 1.f / sum;
-  for (int e = 0; e < E; ++e) {
-    float l = row[e];
-    float p = (l == l) ? expf(l - m) * inv : 0.f;
-    drow[e] = accumulate ? drow[e] - p * s : -p * s;
+  auto dval = [&](float l, float old) {
+    const float p = (l == l) ? expf(l - m) * inv : 0.f;
+    return accumulate ? old - p * s : -p * s;
+  };
+  if ((E & 3) == 0) {  // 16-byte rows: four values per load and store
+    for (int e = 0; e < E; e += 4) {
+      const float4 l = *reinterpret_cast<const float4 *>(row + e);
+      float4 o = {0.f, 0.f, 0.f, 0.f};
+      if (accumulate) o = *reinterpret_cast<const float4 *>(drow + e);
+      *reinterpret_cast<float4 *>(drow + e) =
+          make_float4(dval(l.x, o.x), dval(l.y, o.y), dval(l.z, o.z), dval(l.w, o.w));
+    }
+  } else {
+    for (int e = 0; e < E; ++e) drow[e] = dval(row[e], accumulate ? drow[e] : 0.f);
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
@@ -396,30 +415,27 @@ hipError_t launch_router_logits(const void *x, const void *w_router, const float
 
 template <int KMAX>
 static void launch_topk_k(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *rank, int32_t *blk_cnt,
-                          int64_t T, int E, int k, int bits, bool renorm, hipStream_t s) {
+                          int64_t T, int E, int k, bool renorm, hipStream_t s) {
   dim3 grid((unsigned)route_blocks(T));
-  route_topk_kernel<KMAX><<<grid, 256, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, bits,
-                                               renorm ? 1 : 0);
+  route_topk_kernel<KMAX><<<grid, 256, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, renorm ? 1 : 0);
 }
 
 hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
                         int32_t *offsets, int32_t *row_of_slot, int32_t *src_of_row, int32_t *blk_cnt,
                         int64_t T, int E, int k, bool renorm, hipStream_t s) {
-  int bits = 0;
-  while ((1 << bits) < E) ++bits;
   const int64_t nblk = route_blocks(T);
   {
     LaunchScope scope("route_topk", s);
     if (k <= 1)
-      launch_topk_k<1>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+      launch_topk_k<1>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, renorm, s);
     else if (k <= 2)
-      launch_topk_k<2>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+      launch_topk_k<2>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, renorm, s);
     else if (k <= 4)
-      launch_topk_k<4>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+      launch_topk_k<4>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, renorm, s);
     else if (k <= 8)
-      launch_topk_k<8>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+      launch_topk_k<8>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, renorm, s);
     else
-      launch_topk_k<16>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, bits, renorm, s);
+      launch_topk_k<16>(logits, topk_idx, topk_w, row_of_slot, blk_cnt, T, E, k, renorm, s);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
