@@ -332,38 +332,48 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           if (i != b) continue;
+          // the lane's FN*4 groups of four columns; the h of group q+1 is
+          // read from LDS before group q is computed and written back, so
+          // that the read latency overlaps the arithmetic
+          constexpr int NG = FN * 4;
+          auto goff = [&](int q) {  // element offset of group q in either half
+            const int r = wm * 32 + l32;
+            const int col = wn * WN + (q >> 2) * 32 + 8 * (q & 3) + 4 * lhi;
+            return stg_off(r, col, BN);
+          };
+          uint2 hgn = *reinterpret_cast<const uint2 *>(sg_tile + goff(0));
+          uint2 hun = *reinterpret_cast<const uint2 *>(su_tile + goff(0));
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int r = wm * 32 + l32;
-              const int col = wn * WN + j * 32 + 8 * g + 4 * lhi;
-              uint2 *pg = reinterpret_cast<uint2 *>(sg_tile + stg_off(r, col, BN));
-              uint2 *pu = reinterpret_cast<uint2 *>(su_tile + stg_off(r, col, BN));
-              const uint2 hg2 = *pg, hu2 = *pu;
-              const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
-                                   __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
-              const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
-                                   __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
-              float dg[4], du[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                // t = dA s, dH_up = t hg, dH_gate = t hu (1 + hg (1 - s)) = th + th u
-                // with th = t hu and u = hg - hg s (s = sigmoid(hg))
-                const float sgm = sigmoid_f(hg[q]);
-                const float t = acc[i][j][4 * g + q] * sgm;
-                const float th = t * hu[q];
-                du[q] = t * hg[q];
-                dg[q] = fmaf(th, fmaf(-hg[q], sgm, hg[q]), th);
-              }
-              uint2 og, ou;
-              og.x = pack_bf2(dg[0], dg[1]);
-              og.y = pack_bf2(dg[2], dg[3]);
-              ou.x = pack_bf2(du[0], du[1]);
-              ou.y = pack_bf2(du[2], du[3]);
-              *pg = og;
-              *pu = ou;
+          for (int q = 0; q < NG; ++q) {
+            const uint2 hg2 = hgn, hu2 = hun;
+            if (q + 1 < NG) {
+              hgn = *reinterpret_cast<const uint2 *>(sg_tile + goff(q + 1));
+              hun = *reinterpret_cast<const uint2 *>(su_tile + goff(q + 1));
             }
+            const int j = q >> 2, g = q & 3;
+            const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
+                                 __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
+            const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
+                                 __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
+            float dg[4], du[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              // t = dA s, dH_up = t hg, dH_gate = t hu (1 + hg (1 - s)) = th + th u
+              // with th = t hu and u = hg - hg s (s = sigmoid(hg))
+              const float sgm = sigmoid_f(hg[v]);
+              const float t = acc[i][j][4 * g + v] * sgm;
+              const float th = t * hu[v];
+              du[v] = t * hg[v];
+              dg[v] = fmaf(th, fmaf(-hg[v], sgm, hg[v]), th);
+            }
+            uint2 og, ou;
+            og.x = pack_bf2(dg[0], dg[1]);
+            og.y = pack_bf2(dg[2], dg[3]);
+            ou.x = pack_bf2(du[0], du[1]);
+            ou.y = pack_bf2(du[2], du[3]);
+            *reinterpret_cast<uint2 *>(sg_tile + goff(q)) = og;
+            *reinterpret_cast<uint2 *>(su_tile + goff(q)) = ou;
+          }
         }
       }
       __syncthreads();
