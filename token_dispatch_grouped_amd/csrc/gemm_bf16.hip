@@ -109,32 +109,47 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   if (EPI == EPI_ACC_F32) {
     // acc[i][j][v] sits at tile row wm*WM + i*32 + 8*(v/4) + 4*lhi + (v%4),
-    // tile column wn*WN + j*32 + l32. The 16 old values of a fragment are
-    // loaded together (clamped addresses, so no load waits on a branch),
-    // then the valid ones are written back.
+    // tile column wn*WN + j*32 + l32. Fragment n = i*FN + j is finished as
+    // a group of 16: its old values are loaded together (clamped addresses,
+    // so no load waits on a branch) while fragment n-1 is written back, so
+    // that one group's load latency overlaps the previous group's stores.
     float *C = (float *)p.C + (int64_t)e * p.strideC;
+    constexpr int NGR = FM * FN;
+    auto load_grp = [&](int n, float (&o)[16]) {
+      const int i = n / FN, j = n % FN;
+      const int c = n_tile * BN + wn * WN + j * 32 + l32;
+      const int cc = c < p.N ? c : p.N - 1;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float old[FN][16];
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
+        const int rr = r < m_valid ? r : m_valid - 1;
+        o[v] = C[(int64_t)(m0 + rr) * p.ldc + cc];
+      }
+    };
+    float cur[16], nxt[16];
+    load_grp(0, cur);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n_tile * BN + wn * WN + j * 32 + l32;
-        const int nn = n < p.N ? n : p.N - 1;
+    for (int n = 0; n < NGR; ++n) {
+      if (n + 1 < NGR) load_grp(n + 1, nxt);
+      const int i = n / FN, j = n % FN;
+      const int c = n_tile * BN + wn * WN + j * 32 + l32;
+      // the sums are formed before the conditional stores (the opaque copy
+      // keeps the loads from being moved into the store branches, where each
+      // would wait for every load in flight)
+      float sum[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          const int rr = r < m_valid ? r : m_valid - 1;
-          old[j][v] = C[(int64_t)(m0 + rr) * p.ldc + nn];
-        }
+      for (int v = 0; v < 16; ++v) {
+        sum[v] = cur[v] + acc[i][j][v];
+        asm volatile("" : "+v"(sum[v]));
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n_tile * BN + wn * WN + j * 32 + l32;
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
+        if (r < m_valid && c < p.N) C[(int64_t)(m0 + r) * p.ldc + c] = sum[v];
+      }
+      if (n + 1 < NGR) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (r < m_valid && n < p.N) C[(int64_t)(m0 + r) * p.ldc + n] = old[j][v] + acc[i][j][v];
-        }
+        for (int v = 0; v < 16; ++v) cur[v] = nxt[v];
       }
     }
     return;
