@@ -97,9 +97,9 @@ MOE_DEVICE void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); 
 // offset HALF_OFF, so that the LDS below HALF_OFF can already receive the
 // next tile's first stage; EPI_SWIGLU_FWD stages the whole tile (BM*BN*2
 // bytes) and EPI_SWIGLU_BWD two band buffers (2*BM*BN bytes) from offset 0.
-template <int BM, int BN, int WM, int WN, int EPI, int NT, int HALF_OFF>
+template <int BM, int BN, int WM, int WN, int EPI, int NT, int HALF_OFF, typename NextIssue>
 MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32], u32x4_t *lds, int e, int m0,
-                         int n_tile, int m_valid, int64_t crow0, int wm, int wn) {
+                         int n_tile, int m_valid, int64_t crow0, int wm, int wn, NextIssue issue_next) {
   constexpr int WAVES_M = BM / WM;
   constexpr int FM = WM / 32, FN = WN / 32;
   const int tid = threadIdx.x;
@@ -252,6 +252,10 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
         });
     }
     __syncthreads();
+    // the h tile is out: the first half of its staging area takes the next
+    // tile's first stage (ring slot 0), the second half the a tile
+    issue_next();
+    bf16_t *astg = stg + BM * (BN / 2);
     // staged a = silu(gate) * up tile, BN/2 columns
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -263,13 +267,13 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
           const int col = wn * (WN / 2) + j * 32 + 8 * g + 4 * lhi;
           const f32x16_t &ga = acc[i][j];
           const f32x16_t &ua = acc[i][j + FN / 2];
-          stg_put4(stg, r, col, BN / 2, silu_f(ga[4 * g]) * ua[4 * g], silu_f(ga[4 * g + 1]) * ua[4 * g + 1],
+          stg_put4(astg, r, col, BN / 2, silu_f(ga[4 * g]) * ua[4 * g], silu_f(ga[4 * g + 1]) * ua[4 * g + 1],
                    silu_f(ga[4 * g + 2]) * ua[4 * g + 2], silu_f(ga[4 * g + 3]) * ua[4 * g + 3]);
         }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < WAVES_M; ++h)
-      flush(std::integral_constant<int, BN / 2>{}, stg + h * WM * (BN / 2), h * WM, p.C2, p.F,
+      flush(std::integral_constant<int, BN / 2>{}, astg + h * WM * (BN / 2), h * WM, p.C2, p.F,
             [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
   } else {  // EPI_SWIGLU_BWD: dA -> dH = (dH_gate | dH_up) using the saved h
     // The tile is finished in bands through two LDS buffers, each holding a
@@ -545,9 +549,10 @@ struct NextTile {
 // `pre`: stage 0 of this tile was issued by the previous tile. With a valid
 // `nx` and the plain store epilogue (which leaves ring slot 0 alone), stage 0
 // of the next tile is issued into slot 0 before this tile's epilogue runs.
-template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES,
+          typename NextFn>
 MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_tile, int m_valid, int kdim,
-                        int64_t crow0, const bf16_t *Ab, const bf16_t *Bb, bool pre, const NextTile &nx) {
+                        int64_t crow0, const bf16_t *Ab, const bf16_t *Bb, bool pre, NextFn next_tile) {
   constexpr int NT = NW * 64;
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
@@ -702,16 +707,22 @@ MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_
     interleave();
   }
   __syncthreads();  // every wave is done with the ring before it is reused
-  if (EPI == EPI_STORE) {
-    if (nx.valid) {  // same K; the epilogue below stays clear of slot 0
+  // stage 0 of the next tile (same K) into ring slot 0: the plain store
+  // epilogue stays clear of slot 0 throughout, the SwiGLU forward once its
+  // h tile is out
+  auto issue_next = [&]() {
+    NextTile nx;
+    next_tile(nx);  // decoded only here, so nothing of it is held through the main loop
+    if (nx.valid) {
       OpA na;
       OpB nb;
       init_ops(na, nb, nx.Ab, nx.Bb, nx.m_valid, nx.n_tile);
       na.issue(0, p.lda, kdim, lds0, wave_u);
       nb.issue(0, p.ldb, kdim, lds0 + OpA::BYTES, wave_u);
     }
-  }
-  epilogue<BM, BN, WM, WN, EPI, NT, STAGE_BYTES>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn);
+  };
+  if (EPI == EPI_STORE) issue_next();
+  epilogue<BM, BN, WM, WN, EPI, NT, STAGE_BYTES>(p, acc, lds, e, m0, n_tile, m_valid, crow0, wm, wn, issue_next);
 }
 
 // Grouped GEMM with DMA-fed LDS stages: 2 slots of 64-deep k, the next
@@ -772,15 +783,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
         pre = false;
         continue;
       }
-      NextTile nx;
-      int ne, nm0;
-      int64_t ncrow0;
-      nx.valid = bid + nW < hi && decode(bid + nW, ne, nm0, ncrow0, nx.n_tile, nx.m_valid);
-      nx.Ab = p.A + (nx.valid ? ncrow0 : 0) * p.lda;
-      nx.Bb = p.B + (int64_t)(nx.valid ? ne : 0) * p.strideB;
+      // the next tile of this workgroup, asked for by the epilogues that
+      // issue its first stage early; nvalid reports whether they did
+      bool nvalid = false;
+      auto next_tile = [&](NextTile &nx) {
+        int ne, nm0;
+        int64_t ncrow0;
+        nx.valid = bid + nW < hi && decode(bid + nW, ne, nm0, ncrow0, nx.n_tile, nx.m_valid);
+        nx.Ab = p.A + (nx.valid ? ncrow0 : 0) * p.lda;
+        nx.Bb = p.B + (int64_t)(nx.valid ? ne : 0) * p.strideB;
+        nvalid = nx.valid;
+      };
       gg_tile<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, BK, STAGES>(
-          p, lds, e, m0, n_tile, m_valid, p.K, crow0, p.A + crow0 * p.lda, p.B + (int64_t)e * p.strideB, pre, nx);
-      pre = nx.valid && EPI == EPI_STORE;
+          p, lds, e, m0, n_tile, m_valid, p.K, crow0, p.A + crow0 * p.lda, p.B + (int64_t)e * p.strideB, pre,
+          next_tile);
+      pre = nvalid;
       __syncthreads();  // the epilogue's LDS reads are done before the next tile's DMA
     }
   } else {
@@ -806,7 +823,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
     crow0 = 0;
     Ab = p.A + (int64_t)row0 * p.lda + m0;      // k-major: column m0 at k = 0
     Bb = p.B + (int64_t)row0 * p.ldb;
-    const NextTile none{p.A, p.B, 0, 0, false};
+    auto none = [&](NextTile &nx) { nx.valid = false; };
     gg_tile<BM, BN, WM, WN, NW, AKM, BKM, EPI, RAGGED_K, BK, STAGES>(p, lds, e, m0, n_tile, m_valid, kdim, crow0,
                                                                      Ab, Bb, false, none);
   }
