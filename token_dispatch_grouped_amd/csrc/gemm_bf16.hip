@@ -303,6 +303,7 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
     constexpr int SCH = 2 * BR * CPR / (NT / 2);  // 16-byte chunks per storing thread
     constexpr int SB = 8;                       // chunks read from LDS before storing
     static_assert(2 * BUF <= 160 * 1024, "two band buffers must fit in LDS");
+    static_assert(BUF == HALF_OFF, "band buffer 0 is ring slot 0");
     static_assert(NBAND * BR == BM && NI * RPI * NLW == BR && CPR >= 16, "band shape");
     static_assert(SCH * (NT / 2) == 2 * BR * CPR && SCH % SB == 0 && (NT / 2) % CPR == 0, "store split");
     const int n0 = n_tile * BN;
@@ -345,6 +346,9 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
         else wait_vm<0>();
       }
       __syncthreads();
+      // last band in buffer 1: buffer 0 (ring slot 0) is read out, so the
+      // next tile's first stage can land there meanwhile
+      if (!next && (b & 1)) issue_next();
       bf16_t *sg_tile = stg + (b & 1) * (2 * HALF);  // h_gate -> dH_gate
       bf16_t *su_tile = sg_tile + HALF;             // h_up   -> dH_up
       {
