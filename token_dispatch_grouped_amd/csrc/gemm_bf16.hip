@@ -37,10 +37,12 @@
 // that each lane holds four consecutive output columns); the plain store
 // stages one wavefront row at a time so that the next tile's first stage can
 // land in the other ring slot meanwhile. The SwiGLU forward writes h and
-// a = silu(gate) * up from the fp32 accumulators; the SwiGLU backward loads
-// its h bands into LDS by DMA and rewrites them in place as dH. Weight
-// gradients are read-modify-written in fp32, each element by exactly one
-// workgroup (no atomics).
+// a = silu(gate) * up from the fp32 accumulators, and issues the next
+// tile's first stage once h is out; the SwiGLU backward loads its h bands
+// into LDS by DMA and rewrites them in place as dH, issuing the next tile's
+// first stage during its last band. Weight gradients are read-modify-written
+// in fp32, each element by exactly one workgroup (no atomics), one
+// fragment's old values loading while the previous fragment is stored.
 #include <algorithm>
 
 #include "common.h"
