@@ -57,16 +57,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "7d0c857d6310c834a81f6fb81be97273b62a34517cb28961b2b9cb20626ee353",
+    "sources_sha256": "70ec4092aa1013acde91488064060132fae6e42d7555e7c03018d6e57d59bf7a",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.635 + 2.062) * 2 ** 30,
-        "gg_down_fwd": (2.453 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.579 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.771 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (4.904 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.662 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.904 + 2.064) * 2 ** 30,
+        "gg_down_fwd": (2.425 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.919 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.751 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.931 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.671 + 0.645) * 2 ** 30,
     },
 }
 
