@@ -57,7 +57,7 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "70ec4092aa1013acde91488064060132fae6e42d7555e7c03018d6e57d59bf7a",
+    "sources_sha256": "ae9b0314a09d48835985e904718677831880ef6686991fd8053e8feea9622f02",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30

@@ -552,9 +552,11 @@ struct NextTile {
 };
 
 // One output tile: operand set-up, the DMA-fed main loop and the epilogue.
-// `pre`: stage 0 of this tile was issued by the previous tile. With a valid
-// `nx` and the plain store epilogue (which leaves ring slot 0 alone), stage 0
-// of the next tile is issued into slot 0 before this tile's epilogue runs.
+// `pre`: stage 0 of this tile was issued by the previous tile. next_tile(nx)
+// describes the workgroup's next tile (same K); the epilogues that free ring
+// slot 0 early (plain store: before it starts; SwiGLU forward: once h is
+// out; SwiGLU backward: during a last band held in buffer 1) ask for it
+// there and issue its stage 0 into slot 0.
 template <int BM, int BN, int WM, int WN, int NW, bool AKM, bool BKM, int EPI, bool RAGGED_K, int BK, int STAGES,
           typename NextFn>
 MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_tile, int m_valid, int kdim,
