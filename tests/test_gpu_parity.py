@@ -165,6 +165,12 @@ SMALL_CASES = [
     # F = 64: the down forward is one 64-deep stage, and with d = 2048 its ~560 tiles give every persistent
     # workgroup several, so a tile whose only stage was issued during the previous tile's epilogue runs
     ("bf16_F64_multi_tile", small_workload(4096, 2048, 8, 4, 64, BF16, "zipf", seed=29, n_empty=1), False),
+    # every ragged-M product with more tiles than workgroups (gate/up forward ~2.6 per workgroup, the others
+    # 1.3-1.7) and Zipf tails of every length, so the next tile's first stage is issued from each epilogue
+    # (plain store, SwiGLU forward after h, SwiGLU backward in a last band held in either buffer) and the
+    # whole result is compared, not a sample
+    ("bf16_persistent_all_epilogues", small_workload(6144, 1024, 16, 4, 768, BF16, "zipf", seed=30, n_empty=2),
+     False),
 ]
 
 
