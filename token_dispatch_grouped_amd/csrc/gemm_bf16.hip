@@ -85,6 +85,25 @@ MOE_DEVICE void dma16(const void *g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
 }
 
+// The same 16 bytes per lane through a buffer resource (base, num_records
+// in bytes): lane offsets at or past num_records read zeros. Used for the
+// k-major operands of the weight gradients, whose stage base moves on the
+// scalar side while the lane offsets stay fixed.
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+MOE_DEVICE rsrc_t make_rsrc(const void *base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)base;
+  rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)num_records);
+  r.w = 0x00020000;  // 32-bit data format, untyped access
+  return r;
+}
+MOE_DEVICE void bdma16(rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 template <int N>
 MOE_DEVICE void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -468,7 +487,10 @@ MOE_DEVICE int kc_swz(int r) {
   return CPR == 8 ? swz(r) : ((r >> 2) & 3);
 }
 
-template <int ROWS, bool KM, int NW, int BK>
+// BUF (k-major only): the DMA goes through a buffer resource whose base is
+// the stage's first k row, each lane keeping a 32-bit offset, and k rows past
+// kdim read zeros from the resource's range check instead of being clamped.
+template <int ROWS, bool KM, int NW, int BK, bool BUF = false>
 struct Operand {
   static constexpr int NT = NW * 64;
   static constexpr int BYTES = ROWS * BK * 2;
@@ -478,15 +500,19 @@ struct Operand {
   static constexpr int CPR = ROWB / 16;             // 16-byte chunks per LDS row
   static constexpr int RPI = 1024 / ROWB;           // LDS rows per DMA instruction
   static_assert(!KM || CPR >= 16, "k-major tiles need at least 128 columns");
+  static_assert(!BUF || KM, "buffer DMA is for k-major operands");
 
   const bf16_t *ptr[NDMA];  // KC: source at k = 0; KM: column base of the lane
   int krow[NDMA];           // KM: k row of the lane within a stage
+  const char *kbase;        // BUF: column 0 of the tile at k = 0
+  uint32_t voff[NDMA];      // BUF: byte offset of the lane's 16 bytes from a stage's base
 
   // base: first element of the tile's first row (KC) or of column 0 at k = 0
   // (KM); ld: row pitch; valid: rows (KC) or columns (KM) that exist;
   // row_map(r) (KC only) gives the source row of tile row r.
   template <typename RowMap>
   MOE_DEVICE void init(const bf16_t *base, int64_t ld, int valid, int wave, int lane, RowMap row_map) {
+    kbase = reinterpret_cast<const char *>(base);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int r = (i * NW + wave) * RPI + lane / CPR;
@@ -501,12 +527,20 @@ struct Operand {
         if (col >= valid) col = valid - 8;  // past-the-end columns feed masked outputs only
         ptr[i] = base + col;
         krow[i] = r;
+        voff[i] = (uint32_t)(((int64_t)r * ld + col) * 2);  // r < BK: far below 2^32
       }
     }
   }
   // Issue the DMA of stage data at k0 into LDS byte address `dst` (+ wave's
   // 1 KB slices). KM sources clamp k rows to kdim-1; the tail is zeroed later.
   MOE_DEVICE void issue(int k0, int64_t ld, int kdim, uint32_t dst, int wave) const {
+    if constexpr (BUF) {
+      const int64_t rem = (int64_t)(kdim - k0) * ld * 2;  // bytes of valid rows from k0 on
+      const rsrc_t rs = make_rsrc(kbase + (int64_t)k0 * ld * 2, rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) bdma16(rs, voff[i], dst + (uint32_t)((i * NW + wave) * 1024));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const uint32_t d = dst + (uint32_t)((i * NW + wave) * 1024);
@@ -569,8 +603,8 @@ MOE_DEVICE void gg_tile(const GemmParams &p, u32x4_t *lds, int e, int m0, int n_
   static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
   static_assert(RAGGED_K == (EPI == EPI_ACC_F32), "weight gradients are the ragged-K products");
   constexpr bool SWAP = EPI != EPI_ACC_F32;
-  using OpA = Operand<BM, AKM, NW, BK>;
-  using OpB = Operand<BN, BKM, NW, BK>;
+  using OpA = Operand<BM, AKM, NW, BK, RAGGED_K>;
+  using OpB = Operand<BN, BKM, NW, BK, RAGGED_K>;
   constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
   constexpr int RING_BYTES = STAGES * STAGE_BYTES;
   // staging: one wavefront row in ring slot 1 for EPI_STORE, the whole tile
@@ -747,8 +781,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gg_dma_kernel(GemmParams p) {
   static_assert(EPI != EPI_SWIGLU_FWD || (FN % 2) == 0, "gate/up pairs need an even fragment count");
   static_assert(RAGGED_K == (EPI == EPI_ACC_F32), "weight gradients are the ragged-K products");
   constexpr bool SWAP = EPI != EPI_ACC_F32;
-  using OpA = Operand<BM, AKM, NW, BK>;
-  using OpB = Operand<BN, BKM, NW, BK>;
+  using OpA = Operand<BM, AKM, NW, BK, RAGGED_K>;
+  using OpB = Operand<BN, BKM, NW, BK, RAGGED_K>;
   constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
   constexpr int RING_BYTES = STAGES * STAGE_BYTES;
   // staging: one wavefront row in ring slot 1 for EPI_STORE, the whole tile
