@@ -20,9 +20,9 @@
 // Tiling: a 512-thread workgroup (8 wavefronts, 2 x 4) computes a 256 x 256
 // tile; each wavefront owns a 128 x 64 sub-tile of v_mfma_f32_32x32x16_bf16
 // results held in fp32. k advances 64 at a time through a 2-slot LDS ring
-// filled by the LDS DMA (global_load_lds_dwordx4, tile data never passes
-// through registers): the next stage is in flight while the current one is
-// consumed. k-contiguous operands sit in 128-byte LDS rows with an XOR chunk
+// filled by the LDS DMA (global_load_lds_dwordx4; buffer_load_dwordx4 ... lds
+// for the weight gradients' operands; tile data never passes through
+// registers): the next stage is in flight while the current one is consumed. k-contiguous operands sit in 128-byte LDS rows with an XOR chunk
 // swizzle; k-major operands are copied as they are and read through the
 // transposing ds_read_b64_tr_b16.
 //
