@@ -57,16 +57,16 @@ MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "ae9b0314a09d48835985e904718677831880ef6686991fd8053e8feea9622f02",
+    "sources_sha256": "26df0d780eb7acba45fa54e98f68a4257e29deceb907aa68d1bc026f2041b7af",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.904 + 2.064) * 2 ** 30,
-        "gg_down_fwd": (2.425 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.919 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.751 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (4.931 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.671 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (7.186 + 2.064) * 2 ** 30,
+        "gg_down_fwd": (2.454 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.888 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.709 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (5.048 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.663 + 0.645) * 2 ** 30,
     },
 }
 
