@@ -171,6 +171,10 @@ SMALL_CASES = [
     # whole result is compared, not a sample
     ("bf16_persistent_all_epilogues", small_workload(6144, 1024, 16, 4, 768, BF16, "zipf", seed=30, n_empty=2),
      False),
+    # rows wider than one pass of the combine backward (2048 16-byte chunks per wavefront): d = 16448 in bf16
+    # and d = 8256 in fp32 take a second pass over the row's last chunks
+    ("bf16_wide_d16448", small_workload(6, 16448, 4, 2, 64, BF16, "normal", seed=39), False),
+    ("f32_wide_d8256", small_workload(5, 8256, 3, 2, 64, F32, "normal", seed=40), False),
 ]
 
 

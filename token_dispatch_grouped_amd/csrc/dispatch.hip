@@ -90,8 +90,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
 }
 
 // B1: dy[row] = w[t,j] dout[t];  dtopk_w[t,j] = <dout[t], y[row]>.
-// One wavefront per token: each lane holds CPL chunks of dout, the k dot
-// products are reduced across the wavefront.
+// One wavefront per token: a lane takes CPL chunks of the row per pass
+// (unrolled, all their loads in flight together) and the passes repeat until
+// the whole row is covered, so every width d works; the shapes measured here
+// need one pass. The k dot products are reduced across the wavefront.
 template <typename T, int CPL, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ dout, const T *__restrict__ y,
                                                           const float *__restrict__ tw,
@@ -113,29 +115,31 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ 
   float dot[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) dot[j] = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += CPL * 64) {
 #pragma unroll
-  for (int q = 0; q < CPL; ++q) {
-    const int c = lane + q * 64;
-    if (c >= nc) break;
-    float gv[V];
-    Elem<T>::unpack(ld16_nt(dout + t * ld + (int64_t)c * V), gv);
-    u32x4_t raw[KMAX];
+    for (int q = 0; q < CPL; ++q) {
+      const int c = c0 + lane + q * 64;
+      if (c >= nc) break;
+      float gv[V];
+      Elem<T>::unpack(ld16_nt(dout + t * ld + (int64_t)c * V), gv);
+      u32x4_t raw[KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
-      raw[j] = ok ? ld16_nt(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
-    }
+      for (int j = 0; j < KMAX; ++j) {
+        const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
+        raw[j] = ok ? ld16_nt(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < k && (uint64_t)row[j] < (uint64_t)nrows) {
-        float v[V], o[V];
-        Elem<T>::unpack(raw[j], v);
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k && (uint64_t)row[j] < (uint64_t)nrows) {
+          float v[V], o[V];
+          Elem<T>::unpack(raw[j], v);
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          dot[j] = fmaf(gv[i], v[i], dot[j]);
-          o[i] = w[j] * gv[i];
+          for (int i = 0; i < V; ++i) {
+            dot[j] = fmaf(gv[i], v[i], dot[j]);
+            o[i] = w[j] * gv[i];
+          }
+          st16(dy + row[j] * ld + (int64_t)c * V, Elem<T>::pack(o));
         }
-        st16(dy + row[j] * ld + (int64_t)c * V, Elem<T>::pack(o));
       }
     }
   }
@@ -261,7 +265,7 @@ static void combine_bwd_dispatch(const T *dout, const T *y, const float *tw, con
   else if (cpl <= 4) combine_bwd_c<T, 4>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
   else if (cpl <= 8) combine_bwd_c<T, 8>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
   else if (cpl <= 16) combine_bwd_c<T, 16>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
-  else combine_bwd_c<T, 32>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
+  else combine_bwd_c<T, 32>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);  // several passes past 2048 chunks
 }
 
 hipError_t launch_combine_bwd(const void *dout, const void *y, const float *topk_w, const int32_t *row_of_slot,
