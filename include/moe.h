@@ -33,7 +33,8 @@
  *    stream). The host never waits for the device and never reads device
  *    data; per-expert row counts stay on the device.
  *  - T == 0 (an empty microbatch) returns MOE_OK, launches nothing and writes
- *    nothing; NULL is then accepted for every tensor.
+ *    nothing; NULL is then accepted for every tensor. The one exception is
+ *    moe_aux_loss, which writes the zero losses of the empty microbatch.
  *  - Validation happens on the host before the first launch. A NULL pointer
  *    that must be read or written, a pointer not aligned to 16 bytes, a
  *    shape outside the supported matrix or a short workspace is reported
@@ -74,7 +75,7 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *
  * MOE_FLAG_RECOMPUTE: keep no FFN activations between forward and backward
  * (activation checkpointing of the expert FFN: Add MoE expert parallel
- * training runtime, Summary; no-grad execution: Support pipeline parallelism
+ * training runtime, Major changes; no-grad execution: Support pipeline parallelism
  * in TrainerRank without exposing stage scheduling to callers, Acceptance).
  * moe_grouped_gemm_fwd then takes h = a = NULL, never writes h and keeps a
  * only in its workspace; it is also the forward to use when no backward
@@ -115,7 +116,10 @@ moe_status moe_workspace_size(const moe_shape *shape, size_t *route_ws, size_t *
                               size_t *gemm_bwd_ws);
 
 /*
- * Routing and dispatch tables (the routing half of "EP token dispatch").
+ * Routing and dispatch tables (the routing half of "EP token dispatch", Add
+ * MoE expert parallel training runtime, Major changes; any per-expert count,
+ * zero included, without padding by the caller: Support combined expert and
+ * data parallelism in TrainerRank, Desired behavior).
  *
  * If w_router is non-NULL the logits are computed first,
  *   logits[t,e] = <x[t], w_router[e]> + bias[e]   (fp32 accumulation),
@@ -144,7 +148,8 @@ moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router
                      size_t ws_bytes, moe_stream_t stream);
 
 /*
- * Token dispatch (the data-moving half of "EP token dispatch"):
+ * Token dispatch (the data-moving half of "EP token dispatch", Add MoE expert
+ * parallel training runtime, Major changes):
  *   x_perm[row_of_slot[t,j]] = x[t]     x [T,d] s -> x_perm [R,d] s.
  * Each source row is read once and written k times. No padding rows exist:
  * the buffers hold exactly R rows.
@@ -153,7 +158,8 @@ moe_status moe_permute(const moe_shape *shape, const void *x, const int32_t *row
                        void *x_perm, moe_stream_t stream);
 
 /*
- * Grouped SwiGLU expert FFN ("grouped expert compute"), expert by expert over
+ * Grouped SwiGLU expert FFN ("grouped expert compute", Add MoE expert parallel
+ * training runtime, Major changes), expert by expert over
  * the rows [offsets[e], offsets[e+1]) of x_perm:
  *   h = X_e W_gu[e]^T         [R,2F] s   (saved for the backward)
  *   a = silu(h[:, :F]) * h[:, F:]  [R,F] s   (saved)
@@ -170,7 +176,9 @@ moe_status moe_grouped_gemm_fwd(const moe_shape *shape, const void *x_perm, cons
                                 void *y, void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
- * Weighted combine back to full source order:
+ * Weighted combine back to full source order (outputs are returned in full
+ * source order: Support combined expert and data parallelism in TrainerRank,
+ * Desired behavior):
  *   out[t] = sum_{j<k} topk_w[t,j] * y[row_of_slot[t,j]]    out [T,d] s,
  * summed in fp32 in increasing j and rounded once.
  */
@@ -178,17 +186,23 @@ moe_status moe_unpermute_combine(const moe_shape *shape, const void *y, const fl
                                  const int32_t *row_of_slot, void *out, moe_stream_t stream);
 
 /*
- * Backward of the combine:
+ * Backward of the combine (the backward every microbatch of the canary runs,
+ * whose gradients are compared with a matched reference: Support combined
+ * expert and data parallelism in TrainerRank, Acceptance):
  *   dy[row_of_slot[t,j]] = topk_w[t,j] * dout[t]     dy [R,d] s
  *   dtopk_w[t,j] = <dout[t], y[row_of_slot[t,j]]>   dtopk_w [T,k] fp32
+ * Every row of dy is written (the rows are a permutation of the slots).
  */
 moe_status moe_unpermute_combine_bwd(const moe_shape *shape, const void *dout, const void *y,
                                      const float *topk_w, const int32_t *row_of_slot, void *dy,
                                      float *dtopk_w, moe_stream_t stream);
 
 /*
- * Backward of the routing weights. Selection is piecewise constant, so only
- * the weights carry gradient. With g = dtopk_w and p = softmax(logits[t,:]):
+ * Backward of the routing weights (part of the backward whose model and
+ * expert gradients the canary compares with a matched reference: Support
+ * combined expert and data parallelism in TrainerRank, Acceptance; the router
+ * gradient accumulates like every other: same page, Desired behavior).
+ * Selection is piecewise constant, so only the weights carry gradient. With g = dtopk_w and p = softmax(logits[t,:]):
  *   no renorm: dlogits[t,m] = p_m * (G_m - sum_j topk_w[t,j] g[t,j]),
  *              G_m = g[t,j] if m == topk_idx[t,j] for some j, else 0;
  *   renorm:    dlogits[t,topk_idx[t,j]] = topk_w[t,j] (g[t,j] - sum_j' topk_w g),
@@ -234,7 +248,9 @@ moe_status moe_grouped_gemm_bwd(const moe_shape *shape, const void *dy, const vo
                                 void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
- * Backward of the dispatch:
+ * Backward of the dispatch, returning the token gradient in full source order
+ * (Support combined expert and data parallelism in TrainerRank, Desired
+ * behavior):
  *   dx[t] = sum_j dx_perm[row_of_slot[t,j]] (+ dx_extra[t])    dx [T,d] s,
  * summed in fp32 and rounded once. dx_extra [T,d] fp32 (the router's
  * contribution from moe_route_bwd) may be NULL.
@@ -243,8 +259,9 @@ moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const in
                            const float *dx_extra, void *dx, moe_stream_t stream);
 
 /*
- * MoE auxiliary losses and routing metrics ("MoE losses" and "MoE metrics",
- * Add MoE expert parallel training runtime, Summary and Testing; the pages
+ * MoE auxiliary losses and routing metrics ("MoE metrics" and the "MoE
+ * losses" covered by its regression tests, Add MoE expert parallel training
+ * runtime, Major changes; its test_moe_losses module, Validation; the pages
  * name them without a definition). From the fp32 logits [T,E] of a
  * microbatch and the counts [E] moe_route produced, with p the softmax over
  * all E experts (whatever MOE_FLAG_RENORM says):
@@ -263,7 +280,10 @@ moe_status moe_permute_bwd(const moe_shape *shape, const void *dx_perm, const in
  * overwriting dlogits, or added to it with MOE_AUX_ACCUMULATE. To train a
  * router through moe_route_bwd, call this first and set
  * MOE_FLAG_ACCUMULATE_DLOGITS on the shape. Every token needs a finite
- * logit. All sums run in a fixed order (no atomics). T == 0 writes nothing.
+ * logit. All sums run in a fixed order (no atomics). T == 0 (the empty-work
+ * case, which must contribute zero) writes losses = (0, 0) and metrics all
+ * zero except MOE_METRIC_EMPTY_EXPERTS = E, and no dlogits row; logits,
+ * counts and dlogits may then be NULL.
  * ws: route workspace of at least route_ws bytes.
  * Errors: cfg NULL or a non-finite coefficient -> MOE_ERR_INVALID_ARGUMENT;
  * unknown cfg flag bits -> MOE_ERR_UNSUPPORTED.

@@ -6,7 +6,7 @@ check and the bench's CPU-baseline leg may use it.
 
 What the pages fix and what is read into them
 ---------------------------------------------
-* "Add MoE expert parallel training runtime" (Summary / Major changes) names
+* "Add MoE expert parallel training runtime" (Major changes) names
   the hot path: EP token dispatch followed by grouped expert compute. It gives
   no formulas.
 * "Support combined expert and data parallelism in TrainerRank" (Desired
