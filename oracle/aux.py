@@ -5,8 +5,9 @@ check and the bench's CPU-baseline leg may use it.
 
 What the pages fix and what is read into them
 ---------------------------------------------
-"Add MoE expert parallel training runtime" (Summary and Testing) lists MoE
-losses and MoE metrics among the training features and tests, without
+"Add MoE expert parallel training runtime" lists MoE metrics among the
+training features and MoE losses among the regression coverage (Major
+changes), and runs a MoE-losses test module (Validation), without
 defining either. The readings taken here are the two standard router
 losses and a set of load statistics:
 
@@ -32,7 +33,14 @@ losses and a set of load statistics:
   followed by f_e and P_e for every expert.
 
 Both losses use the softmax over all E experts whatever the renormalisation
-of the routing weights. Defined for T >= 1.
+of the routing weights.
+
+An empty microbatch (T = 0) has to run and contribute zero ("Support
+combined expert and data parallelism in TrainerRank", Acceptance, the
+empty-work case). Its token sums (sum_t lse^2, sum_t p, the counts) are empty
+sums, so the reading taken is: both losses 0, every metric 0 except
+empty_experts = E, f_e = P_e = 0, and no gradient rows. A caller adding the
+losses of several microbatches then adds nothing for the empty one.
 """
 from __future__ import annotations
 
@@ -52,7 +60,9 @@ def _softmax_lse(logits):
 
 
 def aux_losses(logits, counts, k):
-    """(L_bal, L_z) of one microbatch (unweighted)."""
+    """(L_bal, L_z) of one microbatch (unweighted); (0, 0) when T = 0."""
+    if np.asarray(logits).shape[0] == 0:
+        return 0.0, 0.0
     p, lse = _softmax_lse(logits)
     T, E = p.shape
     f = np.asarray(counts, dtype=np.float64) / (T * k)
@@ -72,9 +82,14 @@ def aux_losses_grad(logits, counts, k, alpha, beta):
 
 
 def routing_metrics(logits, counts, k):
-    """Array [5 + 2E]: the five scalars of METRIC_NAMES, then f_e, then P_e."""
+    """Array [5 + 2E]: the five scalars of METRIC_NAMES, then f_e, then P_e.
+    For T = 0: zeros, except empty_experts = E."""
+    T, E = np.asarray(logits).shape
+    if T == 0:
+        out = np.zeros(5 + 2 * E)
+        out[1] = float(E)
+        return out
     p, _ = _softmax_lse(logits)
-    T, E = p.shape
     c = np.asarray(counts, dtype=np.float64)
     mean = T * k / E
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -226,9 +226,13 @@ def test_aux_loss_argument_rules():
     s = shape(T=300, E=16, k=4)
     route_ws, _, _ = moe.moe_workspace_size(s)
     ok = L.make_aux_config(0.01, 1e-3)
-    # T == 0, or nothing requested: no-op with NULLs
+    # T == 0 with no losses or metrics asked for, or nothing requested: no-op with NULLs
     moe.moe_aux_loss(shape(T=0, E=16, k=4), None, None, ok, None, None, None, None, 0, stream=0)
     moe.moe_aux_loss(s, None, None, ok, None, None, None, None, 0, stream=0)
+    # T == 0 writes the zero losses, so its output pointers are validated first
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_aux_loss(shape(T=0, E=16, k=4), None, None, ok, FAKE + 4, None, None, None, 0, stream=0)
+    assert ei.value.status == L.MOE_ERR_MISALIGNED
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_aux_loss(s, FAKE, FAKE, L.make_aux_config(float("nan"), 0.0), FAKE, None, None, FAKE, route_ws,
                          stream=0)

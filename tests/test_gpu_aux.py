@@ -177,3 +177,21 @@ def test_layer_logits_with_aux_losses(renorm):
     lb, lz = oracle.aux_losses(lg, svo["counts"], w.k)
     assert_close("L_bal", to_host64(layer.aux_losses[0:1]), np.array([lb]), TOL_F32)
     assert_close("L_z", to_host64(layer.aux_losses[1:2]), np.array([lz]), TOL_F32)
+
+
+def test_empty_microbatch_writes_zero_losses():
+    """T = 0 (the empty-work case): losses and metrics of the previous call
+    are overwritten with the empty microbatch's values (losses 0, every
+    metric 0 but empty_experts = E), so a caller summing per-microbatch
+    losses adds nothing for it; NULL logits, counts and dlogits are accepted."""
+    import torch
+    import token_dispatch_grouped_amd as m
+    E, k = 12, 3
+    s = m.make_shape(0, 64, E, k, 64, m.MOE_DTYPE_BF16, 0)
+    losses = torch.full((2,), 5.0, device="cuda")
+    metrics = torch.full((m.MOE_METRIC_SCALARS + 2 * E,), 5.0, device="cuda")
+    m.moe_aux_loss(s, None, None, m.make_aux_config(0.01, 0.001), losses, metrics, None, None, 0)
+    torch.cuda.synchronize()
+    want = oracle.routing_metrics(np.zeros((0, E)), np.zeros(E, np.int32), k)
+    assert to_host64(losses).tolist() == list(oracle.aux_losses(np.zeros((0, E)), np.zeros(E, np.int32), k))
+    assert np.array_equal(to_host64(metrics), want)

@@ -110,3 +110,21 @@ def test_minus_infinity_logits():
     assert met[3] == pytest.approx((math.log(4) - 0.75 * math.log(3) + math.log(2)) / 2, rel=1e-14)
     g = oracle.aux_losses_grad(lg, counts, 1, 1.0, 1.0)
     assert np.all(np.isfinite(g)) and g[0, 1] == 0.0 and g[1, 0] == 0.0
+
+
+def test_empty_microbatch_contributes_zero():
+    """An empty microbatch runs and contributes nothing: adding its losses to
+    a per-microbatch sum leaves the sum unchanged; with no tokens every
+    expert has zero rows (empty_experts = E) and the token statistics are
+    empty sums, reported as 0."""
+    rng = np.random.default_rng(5)
+    E, k = 6, 2
+    lg1 = rng.normal(0, 1, (7, E))
+    c1 = np.bincount(np.argsort(-lg1, axis=1, kind="stable")[:, :k].ravel(), minlength=E)
+    empty = np.zeros((0, E))
+    with_empty = np.add(oracle.aux_losses(lg1, c1, k), oracle.aux_losses(empty, np.zeros(E, int), k))
+    assert tuple(with_empty) == oracle.aux_losses(lg1, c1, k)
+    m = oracle.routing_metrics(empty, np.zeros(E, int), k)
+    assert m.shape == (5 + 2 * E,)
+    assert m[1] == E and np.sum(np.zeros(E, int) == 0) == E
+    assert np.all(np.delete(m, 1) == 0.0)

@@ -237,9 +237,25 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(const float *
   }
 }
 
+// An empty microbatch: both losses 0, every metric 0 except the number of
+// empty experts, which is E (no expert has a row).
+__global__ __launch_bounds__(kAuxThreads) void aux_empty_kernel(float *losses, float *metrics, int E) {
+  const int i = threadIdx.x;
+  if (losses && i < 2) losses[i] = 0.f;
+  if (metrics)
+    for (int q = i; q < MOE_METRIC_SCALARS + 2 * E; q += kAuxThreads)
+      metrics[q] = q == MOE_METRIC_EMPTY_EXPERTS ? (float)E : 0.f;
+}
+
 hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *losses, float *metrics, float *dlogits,
                            float *partial, int64_t T, int E, int k, float alpha, float beta, bool accumulate,
                            hipStream_t s) {
+  if (T == 0) {  // no rows of dlogits; the losses and metrics of no tokens
+    if (!losses && !metrics) return hipSuccess;
+    LaunchScope scope("aux_empty", s);
+    aux_empty_kernel<<<1, kAuxThreads, 0, s>>>(losses, metrics, E);
+    return hipGetLastError();
+  }
   const int tpb = aux_tokens_per_block(T);
   const int nblk = (int)((T + tpb - 1) / tpb);
   const float gscale = (float)((double)alpha * E / ((double)T * (double)T * k));

@@ -386,7 +386,16 @@ moe_status moe_aux_loss(const moe_shape *shape, const float *logits, const int32
   st = validate_aux(cfg, &why);
   if (st != MOE_OK) return report(st, why);
   const moe_shape &s = *shape;
-  if (s.T == 0 || (!losses && !metrics && !dlogits)) return MOE_OK;
+  if (!losses && !metrics && (s.T == 0 || !dlogits)) return MOE_OK;
+  if (s.T == 0) {
+    // an empty microbatch contributes zero losses; only the outputs asked for are written
+    const PtrArg outs[] = {{"losses", losses, false, false}, {"metrics", metrics, false, false}};
+    st = validate_ptrs(outs, 2, &why);
+    if (st != MOE_OK) return report(st, why);
+    return hip_status(launch_aux_loss(nullptr, nullptr, losses, metrics, nullptr, nullptr, 0, s.E, s.k,
+                                      cfg->balance_coef, cfg->z_coef, false, as_stream(stream)),
+                      "aux_loss");
+  }
   const PtrArg args[] = {{"logits", logits, true, false},  {"counts", counts, true, false},
                          {"losses", losses, false, false}, {"metrics", metrics, false, false},
                          {"dlogits", dlogits, false, false}};
