@@ -148,6 +148,24 @@ moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router
                      size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * moe_route without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments, results and errors are those of moe_route;
+ * the per-workgroup histograms go to a static scratch array of 4 MiB per GPU
+ * instead (held by each GPU the library runs on until the process ends), so
+ * ceil(T / 256) * E * 4 bytes must fit in it: T up to 1,048,576 tokens at
+ * E = 256, 8,388,608 at E = 32. Larger shapes return MOE_ERR_UNSUPPORTED
+ * before anything is launched. The call allocates no device memory. Every
+ * call on one GPU shares that GPU's scratch: calls that overlap in time on
+ * one GPU (different streams, or different threads) race and may return
+ * wrong tables; calls ordered on one stream do not.
+ */
+moe_status moe_route_noalloc(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                             float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                             int32_t *offsets, int32_t *row_of_slot, int32_t *src_of_row,
+                             moe_stream_t stream);
+
+/*
  * Token dispatch (the data-moving half of "EP token dispatch", Add MoE expert
  * parallel training runtime, Major changes):
  *   x_perm[row_of_slot[t,j]] = x[t]     x [T,d] s -> x_perm [R,d] s.

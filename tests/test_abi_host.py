@@ -81,6 +81,20 @@ def test_empty_microbatch_is_a_noop_with_nulls():
     moe.moe_permute_bwd(s, None, None, None, None, stream=0)
 
 
+def test_route_noalloc_argument_rules():
+    """The allocation-free route validates like moe_route and rejects, before
+    any launch, shapes whose histograms exceed its 4 MiB static scratch."""
+    moe.moe_route_noalloc(shape(T=0), None, None, None, None, None, None, None, None, None, None, stream=0)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_noalloc(shape(T=300), None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "src_of_row" in str(ei.value)
+    # ceil(T/256) * E * 4 bytes: 4097 workgroups of 256 experts is one past the 4 MiB
+    big = shape(T=4097 * 256, E=256, k=8)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_noalloc(big, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED and "static scratch" in str(ei.value)
+
+
 def test_empty_microbatch_still_validates_shape():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_permute(shape(T=0, k=9, E=4), None, None, None, stream=0)

@@ -62,6 +62,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "moe_workspace_size": (ctypes.c_int, [_S, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "moe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_noalloc": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_permute": (ctypes.c_int, [_S, _P, _P, _P, _P]),
     "moe_grouped_gemm_fwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
@@ -155,6 +156,14 @@ def moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, counts, offset
     _check(lib.moe_route(ctypes.byref(shape), ptr(x), ptr(w_router), ptr(bias), ptr(logits), ptr(topk_idx),
                          ptr(topk_w), ptr(counts), ptr(offsets), ptr(row_of_slot), ptr(src_of_row), ptr(ws),
                          int(ws_bytes), _stream(stream)), "moe_route")
+
+
+def moe_route_noalloc(shape, x, w_router, bias, logits, topk_idx, topk_w, counts, offsets, row_of_slot,
+                      src_of_row, stream=None):
+    lib = load()
+    _check(lib.moe_route_noalloc(ctypes.byref(shape), ptr(x), ptr(w_router), ptr(bias), ptr(logits), ptr(topk_idx),
+                                 ptr(topk_w), ptr(counts), ptr(offsets), ptr(row_of_slot), ptr(src_of_row),
+                                 _stream(stream)), "moe_route_noalloc")
 
 
 def moe_permute(shape, x, row_of_slot, x_perm, stream=None):

@@ -44,6 +44,9 @@ hipError_t launch_router_logits(const void *x, const void *w_router, const float
 hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,
                         int32_t *offsets, int32_t *row_of_slot, int32_t *src_of_row, int32_t *blk_cnt,
                         int64_t T, int E, int k, bool renorm, hipStream_t s);
+// Device address of the current GPU's static routing scratch
+// (kRouteScratchBytes), looked up once per device.
+hipError_t route_scratch(int32_t **out);
 hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
                             const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
                             bool accumulate, hipStream_t s);

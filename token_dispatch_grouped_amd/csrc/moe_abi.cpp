@@ -9,6 +9,7 @@
 // uneven or empty work never needs special handling by the caller (same page,
 // Desired behavior and Acceptance).
 #include <hip/hip_runtime.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <cmath>
@@ -179,6 +180,53 @@ moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router
     if (st != MOE_OK) return st;
   }
   int32_t *blk_cnt = reinterpret_cast<int32_t *>(ws);
+  return hip_status(launch_route(logits, topk_idx, topk_w, counts, offsets, row_of_slot, src_of_row, blk_cnt, s.T,
+                                 s.E, s.k, (s.flags & MOE_FLAG_RENORM) != 0, hs),
+                    "route");
+}
+
+moe_status moe_route_noalloc(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                             float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets,
+                             int32_t *row_of_slot, int32_t *src_of_row, moe_stream_t stream) {
+  moe::AbiRange range("moe_route_noalloc");
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (s.T == 0) return MOE_OK;
+  const bool router = w_router != nullptr;
+  const PtrArg args[] = {
+      {"x", x, router, !router},
+      {"w_router", w_router, false, false},
+      {"bias", bias, false, !router},
+      {"logits", logits, true, false},
+      {"topk_idx", topk_idx, true, false},
+      {"topk_w", topk_w, true, false},
+      {"counts", counts, true, false},
+      {"offsets", offsets, true, false},
+      {"row_of_slot", row_of_slot, true, false},
+      {"src_of_row", src_of_row, true, false},
+  };
+  st = validate_ptrs(args, sizeof(args) / sizeof(args[0]), &why);
+  if (st != MOE_OK) return report(st, why);
+  const WorkspaceLayout w = workspace_layout(s);
+  if (w.route_blk_cnt > kRouteScratchBytes) {
+    char buf[200];
+    snprintf(buf, sizeof buf,
+             "moe_route_noalloc: T=%lld, E=%d needs %zu bytes of routing scratch; the static scratch holds %zu "
+             "(use moe_route with a workspace)",
+             (long long)s.T, s.E, w.route_blk_cnt, kRouteScratchBytes);
+    return report(MOE_ERR_UNSUPPORTED, buf);
+  }
+  int32_t *blk_cnt = nullptr;
+  st = hip_status(route_scratch(&blk_cnt), "moe_route_noalloc (scratch address)");
+  if (st != MOE_OK) return st;
+  hipStream_t hs = as_stream(stream);
+  const bool bf16 = s.dtype == MOE_DTYPE_BF16;
+  if (router) {
+    st = hip_status(launch_router_logits(x, w_router, bias, logits, s.T, s.d, s.E, bf16, hs), "router_logits");
+    if (st != MOE_OK) return st;
+  }
   return hip_status(launch_route(logits, topk_idx, topk_w, counts, offsets, row_of_slot, src_of_row, blk_cnt, s.T,
                                  s.E, s.k, (s.flags & MOE_FLAG_RENORM) != 0, hs),
                     "route");

@@ -10,6 +10,8 @@
 // descending, equal logits to the lower expert id; weights are the softmax
 // probabilities of the selected experts (optionally renormalised); rows of
 // one expert follow ascending source token.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -418,6 +420,34 @@ static void launch_topk_k(const float *logits, int32_t *topk_idx, float *topk_w,
                           int64_t T, int E, int k, bool renorm, hipStream_t s) {
   dim3 grid((unsigned)route_blocks(T));
   route_topk_kernel<KMAX><<<grid, 256, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, renorm ? 1 : 0);
+}
+
+// Scratch of the allocation-free routing entry point (moe_route_noalloc):
+// the per-workgroup expert histograms, kRouteScratchBytes in device memory
+// that every GPU the library runs on holds until the process ends. In host
+// code `scratch` names a host-side stand-in, not a device address: the
+// kernels only ever get the address hipGetSymbolAddress returns for the
+// current device. The route pass writes every histogram entry it reads, so
+// nothing has to be cleared between calls.
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+hipError_t route_scratch(int32_t **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    addr[dev] = static_cast<int32_t *>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *counts,

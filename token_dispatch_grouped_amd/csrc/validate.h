@@ -19,6 +19,9 @@ constexpr int kGemmBN = 256;            // bf16 grouped GEMM columns per tile
 constexpr int kGemmGroupM = 4;          // row tiles per group in the ragged-M tile order
 constexpr int kGemmF32Tile = 16;        // fp32 grouped GEMM tile edge
 constexpr int kAuxMaxBlocks = 1024;     // partial rows of the auxiliary-loss pass
+// Static per-GPU scratch of moe_route_noalloc: the per-workgroup expert
+// histograms of the route pass, ceil(T / kRouteTokens) * E int32.
+constexpr size_t kRouteScratchBytes = (size_t)4 << 20;
 
 struct WorkspaceLayout {
   size_t route_blk_cnt;   // bytes of the per-workgroup expert histograms
