@@ -45,9 +45,14 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     quiet NaN pattern so that they stay NaN.
     """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (the largest,
+    # -inf = 0xFF800000, gains at most 0x8000); NaNs are overwritten below
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    r = r.astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         r[nan] = np.uint16(0x7FC0)
