@@ -24,6 +24,16 @@ step over its time. The default (``train``) is the headline measurement.
 (fp32 masters and moments, bf16 working copies written in place, gradients
 zeroed in the same pass) to every training step; its kernel is reported as
 ``adamw`` with 34 bytes per weight element.
+
+With the default workload (ep_share_32k) the line also carries
+``other_32k_workloads``: the empty-microbatch accumulation run and the d=4096
+uniform and Zipf shares, each timed the same way over ``--other-steps``
+steps (ms/step, layer TFLOP/s, grouped-GEMM % of peak, permute/combine GB/s,
+per-kernel times). ``attainable`` holds the rates the library's probes reach
+on this GPU (a bf16 MFMA loop from registers and a 1 GiB device copy); every
+GEMM and memory kernel is also reported as a percentage of those
+(``pct_attainable``). Routing kernels report GB/s on their algorithmic bytes
+(fp32 logits and int32 tables).
 """
 from __future__ import annotations
 
@@ -116,6 +126,11 @@ def parse():
                          "to the forward and their gradient to the backward")
     ap.add_argument("--optimizer", action="store_true",
                     help="append the fused AdamW update of the expert weights to every step (train/recompute)")
+    ap.add_argument("--other-steps", type=int, default=10,
+                    help="timed steps of each other 32k-token workload (microbatches_32k, large_share_uniform, "
+                         "large_share_zipf) measured after the default ep_share_32k one; 0 skips them")
+    ap.add_argument("--no-attainable", dest="attainable", action="store_false",
+                    help="skip the MFMA-loop and copy probes of the attainable peaks")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes before timing (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -178,31 +193,73 @@ def cpu_baseline(w, inp, target_s, fwd_only=False):
                       f"of the same inputs ({dt:.1f} s)"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this library models one expert-parallel rank's local share "
-              "on a single MI355X and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def route_bytes(name, T, E, k, nblk, renorm=False):
+    """Algorithmic HBM bytes of one launch of a routing kernel (fp32 logits,
+    int32 tables), or None for a kernel without a model."""
+    if name == "route_topk":      # logits in; ids, weights, in-workgroup ranks out; histograms out
+        return T * (4 * E + 12 * k) + 4 * nblk * E
+    if name == "route_scan":      # histograms scanned in place; counts out
+        return 8 * nblk * E + 4 * E
+    if name == "route_rows":      # ids and ranks in (+ the histogram table once); rows and inverse out
+        return 16 * T * k + 4 * nblk * E + 8 * E
+    if name == "route_bwd":       # dtopk_w, ids, weights in; logits in (no renorm); dlogits out
+        return T * ((4 if renorm else 8) * E + 12 * k)
+    return None
 
+
+def attainable_peaks(dev):
+    """Rates measured on this GPU by the library's probes: the bf16 MFMA loop
+    (best of three ~5 ms launches) and a 2 x 1 GiB device copy (median of
+    ten), each timed with HIP events on the launch stream."""
+    import torch
+    import token_dispatch_grouped_amd as moe
+    stream = torch.cuda.current_stream()
+    out = torch.empty(moe.moe_peak_mfma_size(), dtype=torch.float32, device=dev)
+    best = 0.0
+    for i in range(4):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        fl = moe.moe_peak_mfma(out, 40000)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if i:  # the first launch warms up
+            best = max(best, fl / (ev0.elapsed_time(ev1) * 1e-3) / 1e12)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rates = []
+    for i in range(13):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        moe.moe_peak_copy(src, dst, nbytes)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            rates.append(2 * nbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
+    del src, dst, out
+    torch.cuda.empty_cache()
+    rates.sort()
+    return {"mfma_bf16_tflops": round(best, 1), "copy_GBps": round(rates[len(rates) // 2], 1),
+            "mfma_probe": "v_mfma_f32_32x32x16_bf16 from registers, 2 wavefronts per SIMD x 4 accumulator chains",
+            "copy_probe": f"16-byte non-temporal device copy of {nbytes >> 20} MiB (2x that in HBM traffic)"}
+
+
+def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
+    """Warm up, then time K steps of the workload without instrumentation and
+    K more with per-kernel events. Returns the line's fields."""
     import numpy as np
     import torch
 
     import token_dispatch_grouped_amd as moe
     from token_dispatch_grouped_amd.layer import MoeLayer
-    from workloads import BF16, F32, WORKLOADS, make_inputs
+    from workloads import BF16, F32, make_inputs
 
-    w = WORKLOADS[args.workload]
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    moe.load()
-
     t_gen = time.perf_counter()
     inp = make_inputs(w)
     t_gen = time.perf_counter() - t_gen
 
-    def dev_t(a, dtype):
+    def dev_t(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
@@ -210,17 +267,18 @@ def main():
     dt = moe.MOE_DTYPE_BF16 if w.dtype == BF16 else moe.MOE_DTYPE_F32
     router = w.routing == "router"
     Tmax = max(max(w.microbatches), 1)
+    torch.cuda.reset_peak_memory_stats(dev)
     layer = MoeLayer(Tmax, w.d, w.E, w.k, w.F, dt, renorm=args.renorm, router=router,
                      recompute=args.mode != "train", aux=(0.01, 1e-3) if args.aux else None)
     W = inp["weights"]
-    wgu, wdn = dev_t(W["w_gu"], w.dtype), dev_t(W["w_down"], w.dtype)
-    wr = dev_t(W["w_router"], w.dtype) if router else None
-    bias = dev_t(W["bias"], F32) if router else None
+    wgu, wdn = dev_t(W["w_gu"]), dev_t(W["w_down"])
+    wr = dev_t(W["w_router"]) if router else None
+    bias = dev_t(W["bias"]) if router else None
     mbs = []
     for mb in inp["micro"]:
         T = mb["x"].shape[0]
-        mbs.append(dict(T=T, x=dev_t(mb["x"], w.dtype), dout=dev_t(mb["dout"], w.dtype),
-                        logits=None if router else dev_t(np.ascontiguousarray(mb["logits"]), F32)))
+        mbs.append(dict(T=T, x=dev_t(mb["x"]), dout=dev_t(mb["dout"]),
+                        logits=None if router else dev_t(np.ascontiguousarray(mb["logits"]))))
     dw_gu = torch.zeros(w.E, 2 * w.F, w.d, dtype=torch.float32, device=dev)
     dw_dn = torch.zeros(w.E, w.d, w.F, dtype=torch.float32, device=dev)
     dw_r = torch.zeros(w.E, w.d, dtype=torch.float32, device=dev) if router else None
@@ -249,7 +307,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -264,7 +322,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             step()
         ev1.record(stream)
         torch.cuda.synchronize()
@@ -277,33 +335,41 @@ def main():
     stream_ms, wall = timed(False)
     prof_ms, _ = timed(True)
     kern = moe.moe_profiler_read_all()
-    ms_per_step = stream_ms / args.steps
+    ms_per_step = stream_ms / steps
 
     flops_step = w.flops_fwd() if nograd else w.flops_fwd_bwd()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     s = 2 if w.dtype == BF16 else 4
     peak = PEAK_BF16_TFLOPS if w.dtype == BF16 else PEAK_F32_TFLOPS
+    att_tf = attain["mfma_bf16_tflops"] if attain and w.dtype == BF16 else None
+    att_bw = attain["copy_GBps"] if attain else None
 
     kernels = {}
     for name, (n, ms) in kern.items():
         avg = ms / max(n, 1)
-        entry = {"launches": n, "avg_ms": round(avg, 5), "total_ms_per_step": round(ms / args.steps, 4)}
+        entry = {"launches": n, "avg_ms": round(avg, 5), "total_ms_per_step": round(ms / steps, 4)}
         base = name.replace("_f32", "")
+        by = None
         if base in GEMM_KERNELS:
             fl_step = sum(GEMM_KERNELS[base] * mb["T"] * w.k * w.d * w.F for mb in mbs)
-            launches_step = max(1, n // args.steps)
-            tf = fl_step / (ms / args.steps * 1e-3) / 1e12
+            launches_step = max(1, n // steps)
+            tf = fl_step / (ms / steps * 1e-3) / 1e12
             entry.update(tflops=round(tf, 2), pct_peak=round(100 * tf / peak, 2),
                          flops_per_launch=fl_step / launches_step)
+            if att_tf:
+                entry["pct_attainable"] = round(100 * tf / att_tf, 2)
         elif name in MEM_KERNELS:
             by = sum(mem_bytes(name, mb["T"], w.d, w.k, s, router) for mb in mbs)
-            gbps = by / (ms / args.steps * 1e-3) / 1e9
-            entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
         elif name == "adamw":
             # theta, grad, m, v read; theta, m, v, bf16 copy, zeroed grad written
             by = 3 * w.E * w.F * w.d * (28 + (2 if w.dtype == BF16 else 0) + 4)
-            gbps = by / (ms / args.steps * 1e-3) / 1e9
+        elif route_bytes(name, 1, w.E, w.k, 1) is not None:
+            by = sum(route_bytes(name, mb["T"], w.E, w.k, -(-mb["T"] // 256), args.renorm) for mb in mbs if mb["T"])
+        if by is not None:
+            gbps = by / (ms / steps * 1e-3) / 1e9
             entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
+            if att_bw:
+                entry["pct_attainable"] = round(100 * gbps / att_bw, 2)
         kernels[name] = entry
 
     gemm_names = [n for n in kernels if n.replace("_f32", "") in GEMM_KERNELS]
@@ -312,9 +378,14 @@ def main():
     mem_names = [n for n in kernels if n in MEM_KERNELS]
     mem_ms = sum(kernels[n]["total_ms_per_step"] for n in mem_names)
     mem_by = sum(mem_bytes(n, mb["T"], w.d, w.k, s, router) for n in mem_names for mb in mbs)
+    route_names = [n for n in kernels if route_bytes(n, 1, w.E, w.k, 1) is not None]
+    route_ms = sum(kernels[n]["total_ms_per_step"] for n in route_names)
+    route_by = sum(route_bytes(n, mb["T"], w.E, w.k, -(-mb["T"] // 256), args.renorm)
+                   for n in route_names for mb in mbs if mb["T"])
     # executed GEMM FLOPs (the recompute product included) over GEMM time
     gemm_tf = gemm_fl / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
     pc_gbps = mem_by / (mem_ms * 1e-3) / 1e9 if mem_ms else 0.0
+    route_gbps = route_by / (route_ms * 1e-3) / 1e9 if route_ms else 0.0
 
     # dominant kernel: largest share of the step
     # among the kernels with a roofline model (grouped GEMMs, dispatch/combine)
@@ -328,39 +399,107 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": None if tr is None else round(tr),
                 "work_per_launch": f"{GEMM_KERNELS[dbase]}*R*d*F = {per_launch:.4g} FLOP"}
+        if att_tf:
+            roof["frac_of_attainable"] = round(ach / att_tf, 4)
     else:
         per_launch = sum(mem_bytes(dom, mb["T"], w.d, w.k, s, router) for mb in mbs) / max(1, kernels[dom][
-            "launches"] // args.steps)
+            "launches"] // steps)
         ach = per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None}
+        if att_bw:
+            roof["frac_of_attainable"] = round(ach / att_bw, 4)
 
     # the recompute product is work done beyond the method's own FLOPs
     executed_fl = flops_step + (GEMM_KERNELS["gg_gateup_recompute"] * sum(mb["T"] for mb in mbs) * w.k * w.d * w.F
                                 if args.mode == "recompute" else 0.0)
-    cfg = {"workload": w.name, "seed": w.seed, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d, "E_local": w.E,
-           "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "mode": args.mode,
-           "optimizer": "adamw" if opt is not None else None, "aux_losses": bool(args.aux),
-           "description": w.description}
-    line = {
-        "metric": METRIC_NOGRAD if nograd else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.dtype == BF16 else "f32", "data": "synthetic",
-        "config": cfg,
+    res = {
+        "value": round(value, 2), "ms_per_step": round(ms_per_step, 4), "steps": steps, "warmup": warmup,
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "grouped_gemm_tflops": round(gemm_tf, 2),
         "grouped_gemm_pct_peak": round(100 * gemm_tf / peak, 2),
         "permute_combine_GBps": round(pc_gbps, 1),
         "permute_combine_pct_hbm": round(100 * pc_gbps / PEAK_HBM_GBPS, 2),
+        "route_GBps": round(route_gbps, 1),
+        "route_pct_hbm": round(100 * route_gbps / PEAK_HBM_GBPS, 2),
         "executed_tflops": round(executed_fl / (ms_per_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
-        "ms_per_step_with_kernel_events": round(prof_ms / args.steps, 4),
+        "ms_per_step_with_kernel_events": round(prof_ms / steps, 4),
         "device_memory_GB": round(torch.cuda.max_memory_allocated(dev) / 1e9, 2),
-        "host_cpu": host_cpu_model(),
         "input_gen_s": round(t_gen, 2),
         "kernels": kernels,
         "roofline": roof,
     }
+    if att_tf:
+        res["grouped_gemm_pct_attainable"] = round(100 * gemm_tf / att_tf, 2)
+    if att_bw:
+        res["permute_combine_pct_attainable"] = round(100 * pc_gbps / att_bw, 2)
+    del layer, mbs, wgu, wdn, wr, bias, dw_gu, dw_dn, dw_r, opt
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, (inp if keep_inputs else None)
+
+
+# the other 32k-token workloads, timed after the headline one in the default run
+OTHER_32K = ("microbatches_32k", "large_share_uniform", "large_share_zipf")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library models one expert-parallel rank's local share "
+              "on a single MI355X and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import token_dispatch_grouped_amd as moe
+    from workloads import BF16, WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.load()
+
+    attain = attainable_peaks(dev) if args.attainable else None
+    res, inp = measure(w, args, args.steps, args.warmup, attain, keep_inputs=args.cpu_seconds > 0)
+
+    nograd = args.mode == "nograd"
+    cfg = {"workload": w.name, "seed": w.seed, "T": list(w.microbatches) if w.micro_T else w.T, "d": w.d,
+           "E_local": w.E, "k": w.k, "F": w.F, "routing": w.routing, "renorm": bool(args.renorm), "mode": args.mode,
+           "optimizer": "adamw" if args.optimizer and not nograd else None, "aux_losses": bool(args.aux),
+           "description": w.description}
+    line = {
+        "metric": METRIC_NOGRAD if nograd else METRIC, "value": res.pop("value"), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": res.pop("steps"), "warmup": res.pop("warmup"), "ms_per_step": res.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == BF16 else "f32", "data": "synthetic", "config": cfg,
+    }
+    line.update(res)
+    line["host_cpu"] = host_cpu_model()
+    line["attainable"] = attain
+
+    # the other 32k-token workloads (empty-microbatch accumulation, d = 4096
+    # uniform and Zipf) under the same clock, fewer steps each
+    if args.other_steps > 0 and w.name == "ep_share_32k":
+        others = {}
+        for name in OTHER_32K:
+            ow = WORKLOADS[name]
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            r, _ = measure(ow, args, args.other_steps, min(args.warmup, 3), attain)
+            keep = ("value", "ms_per_step", "steps", "grouped_gemm_tflops", "grouped_gemm_pct_peak",
+                    "grouped_gemm_pct_attainable", "permute_combine_GBps", "permute_combine_pct_hbm",
+                    "permute_combine_pct_attainable", "route_GBps", "route_pct_hbm", "device_memory_GB")
+            o = {k: r[k] for k in keep if k in r}
+            o["T"] = list(ow.microbatches) if ow.micro_T else ow.T
+            o["d"], o["E_local"], o["F"] = ow.d, ow.E, ow.F
+            o["kernels"] = {n: {k: v for k, v in e.items() if k in ("avg_ms", "total_ms_per_step", "tflops", "GBps",
+                                                                     "pct_peak")}
+                            for n, e in r["kernels"].items()}
+            others[name] = o
+        line["other_32k_workloads"] = others
+
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, fwd_only=nograd)
     else:

@@ -1,6 +1,6 @@
 """Host-side tests of the C ABI (CPU only, no GPU needed).
 
-* the shared library loads and exports every function include/moe.h declares;
+* the shared library loads and exports every function include/*.h declares;
 * argument validation returns the documented status before anything is
   launched (so these calls are safe without a GPU);
 * T == 0 is a successful no-op that accepts NULL tensors;
@@ -10,6 +10,7 @@
   table of cases (host code only).
 """
 import ctypes
+import glob
 import os
 import re
 import shutil
@@ -21,12 +22,12 @@ import token_dispatch_grouped_amd as moe
 from token_dispatch_grouped_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 CSRC = os.path.join(ROOT, "token_dispatch_grouped_amd", "csrc")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
 
@@ -36,9 +37,26 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert len(names) >= 14
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     # and the binding wraps each of them
     assert set(names) <= set(L.exported_names())
+
+
+def test_peak_probe_argument_rules():
+    """The attainable-peak probes reject bad arguments before any launch."""
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_peak_mfma(FAKE, 0, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_peak_mfma(FAKE + 4, 10, stream=0)
+    assert ei.value.status == L.MOE_ERR_MISALIGNED
+    for src, dst, n, st in ((FAKE, FAKE + (1 << 12), 100, L.MOE_ERR_INVALID_ARGUMENT),
+                            (FAKE, FAKE + 16, 4096, L.MOE_ERR_INVALID_ARGUMENT),   # overlap
+                            (FAKE + 8, FAKE + (1 << 16), 4096, L.MOE_ERR_MISALIGNED),
+                            (None, FAKE, 4096, L.MOE_ERR_INVALID_ARGUMENT)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_peak_copy(src, dst, n, stream=0)
+        assert ei.value.status == st
 
 
 def test_version_and_status_strings():

@@ -59,3 +59,13 @@ def test_cpu_baseline_object():
     assert "oracle" in cb["sample"] and "96" in cb["sample"]
     cbf = bench.cpu_baseline(w, make_inputs(w), target_s=0.05, fwd_only=True)
     assert "forward of" in cbf["sample"]
+
+
+def test_route_bytes():
+    T, E, k = 32768, 32, 8
+    nblk = T // 256
+    assert bench.route_bytes("route_topk", T, E, k, nblk) == T * (4 * E + 12 * k) + 4 * nblk * E
+    assert bench.route_bytes("route_bwd", T, E, k, nblk) == T * (8 * E + 12 * k)
+    assert bench.route_bytes("route_bwd", T, E, k, nblk, renorm=True) == T * (4 * E + 12 * k)
+    assert bench.route_bytes("route_rows", T, E, k, nblk) == 16 * T * k + 4 * nblk * E + 8 * E
+    assert bench.route_bytes("gg_gateup_fwd", T, E, k, nblk) is None

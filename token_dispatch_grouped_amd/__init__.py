@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     MOE_ADAMW_ZERO_GRAD, make_adamw_config, moe_adamw_config, moe_adamw_step,
     MOE_FLAG_ACCUMULATE_DLOGITS, MOE_AUX_ACCUMULATE, MOE_METRIC_IMBALANCE, MOE_METRIC_EMPTY_EXPERTS,
     MOE_METRIC_COUNT_CV, MOE_METRIC_ENTROPY, MOE_METRIC_MAX_PROB, MOE_METRIC_SCALARS, make_aux_config,
-    moe_aux_config, moe_aux_loss,
+    moe_aux_config, moe_aux_loss, moe_peak_mfma, moe_peak_mfma_size, moe_peak_copy,
 )
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "load", "make_shape",

@@ -80,6 +80,10 @@ _SIGNATURES = {
     "moe_profiler_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
     "moe_version": (ctypes.c_char_p, []),
+    # include/moe_peak.h
+    "moe_peak_mfma": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _P]),
+    "moe_peak_mfma_size": (ctypes.c_int64, []),
+    "moe_peak_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -233,6 +237,21 @@ def moe_adamw_step(cfg, n, param, grad, exp_avg, exp_avg_sq, param_bf16=None, st
     lib = load()
     _check(lib.moe_adamw_step(ctypes.byref(cfg), int(n), ptr(param), ptr(grad), ptr(exp_avg), ptr(exp_avg_sq),
                               ptr(param_bf16), _stream(stream)), "moe_adamw_step")
+
+
+def moe_peak_mfma_size() -> int:
+    return int(load().moe_peak_mfma_size())
+
+
+def moe_peak_mfma(out, iters: int, stream=None) -> float:
+    """Launch the bf16 MFMA loop; returns the FLOPs of the launch."""
+    fl = ctypes.c_double()
+    _check(load().moe_peak_mfma(ptr(out), int(iters), ctypes.byref(fl), _stream(stream)), "moe_peak_mfma")
+    return fl.value
+
+
+def moe_peak_copy(src, dst, nbytes: int, stream=None):
+    _check(load().moe_peak_copy(ptr(src), ptr(dst), int(nbytes), _stream(stream)), "moe_peak_copy")
 
 
 def moe_status_string(status: int) -> str:

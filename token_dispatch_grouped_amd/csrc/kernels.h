@@ -110,4 +110,11 @@ hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *lo
                            float *partial, int64_t T, int E, int k, float alpha, float beta, bool accumulate,
                            hipStream_t s);
 
+// Attainable-peak probes (peak.hip): a bf16 MFMA loop on `cus` compute
+// units and a plain device copy.
+int peak_mfma_threads(int cus);
+double peak_mfma_flops(int cus, int iters);
+hipError_t launch_peak_mfma(float *out, int cus, int iters, hipStream_t s);
+hipError_t launch_peak_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
+
 }  // namespace moe

@@ -19,6 +19,7 @@
 #include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "moe.h"
+#include "moe_peak.h"
 #include "kernels.h"
 #include "validate.h"
 
@@ -491,6 +492,40 @@ moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, 
   a.scale = cfg->grad_scale;
   a.zero_grad = (cfg->flags & MOE_ADAMW_ZERO_GRAD) != 0;
   return hip_status(launch_adamw(a, as_stream(stream)), "adamw_step");
+}
+
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+int64_t moe_peak_mfma_size(void) {
+  const int cus = device_cus();
+  return cus > 0 ? (int64_t)peak_mfma_threads(cus) : 0;
+}
+
+moe_status moe_peak_mfma(float *out, int32_t iters, double *flops, moe_stream_t stream) {
+  if (!out || !flops) return report(MOE_ERR_INVALID_ARGUMENT, "moe_peak_mfma: out and flops are required");
+  if (iters < 1) return report(MOE_ERR_INVALID_ARGUMENT, "moe_peak_mfma: iters < 1");
+  if (((uintptr_t)out & 15u) != 0) return report(MOE_ERR_MISALIGNED, "moe_peak_mfma: out is not 16-byte aligned");
+  const int cus = device_cus();
+  if (cus <= 0) return report(MOE_ERR_HIP, "moe_peak_mfma: no device");
+  *flops = peak_mfma_flops(cus, iters);
+  return hip_status(launch_peak_mfma(out, cus, iters, as_stream(stream)), "peak_mfma");
+}
+
+moe_status moe_peak_copy(const void *src, void *dst, int64_t bytes, moe_stream_t stream) {
+  if (!src || !dst) return report(MOE_ERR_INVALID_ARGUMENT, "moe_peak_copy: src and dst are required");
+  if (bytes <= 0 || bytes % 16 != 0)
+    return report(MOE_ERR_INVALID_ARGUMENT, "moe_peak_copy: bytes must be a positive multiple of 16");
+  if ((((uintptr_t)src | (uintptr_t)dst) & 15u) != 0)
+    return report(MOE_ERR_MISALIGNED, "moe_peak_copy: src or dst is not 16-byte aligned");
+  const char *s0 = static_cast<const char *>(src), *d0 = static_cast<const char *>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return report(MOE_ERR_INVALID_ARGUMENT, "moe_peak_copy: buffers overlap");
+  if (bytes / 16 > (int64_t)0xffffffff * 256) return report(MOE_ERR_UNSUPPORTED, "moe_peak_copy: too many bytes");
+  return hip_status(launch_peak_copy(src, dst, bytes, as_stream(stream)), "peak_copy");
 }
 
 moe_status moe_profiler_enable(int on) {
