@@ -22,11 +22,14 @@ namespace moe {
 // kernels (combine, un-permute backward) read their rows and write their
 // outputs with non-temporal accesses: each byte is touched once (measured
 // 15-25% faster); the scattering ones keep normal stores, whose rows the
-// grouped GEMM reads next.
+// grouped GEMM reads next (non-temporal stores there measured up to 16%
+// slower for the permute in the layer's step, and 2-4% for the combine
+// backward).
 
 // A4: x_perm[row_of_slot[t,j]] = x[t]. Each source chunk is read once and
 // written k times; a thread copies chunks c and c + nc/2 of one token (nc is
-// even: d is a multiple of 64), which keeps twice the stores in flight.
+// even: d is a multiple of 64), which keeps twice the stores in flight (one
+// chunk per thread, or two adjacent ones, measured slower).
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void permute_kernel(const T *__restrict__ x, const int32_t *__restrict__ ros,
                                                       T *__restrict__ xp, int64_t ntok, int nc, int k) {
@@ -90,10 +93,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
 }
 
 // B1: dy[row] = w[t,j] dout[t];  dtopk_w[t,j] = <dout[t], y[row]>.
-// One wavefront per token: a lane takes CPL chunks of the row per pass
-// (unrolled, all their loads in flight together) and the passes repeat until
-// the whole row is covered, so every width d works; the shapes measured here
-// need one pass. The k dot products are reduced across the wavefront.
+// Rows of fewer than 256 chunks: one wavefront per token, a lane taking CPL
+// chunks of the row per pass (unrolled, all their loads in flight together;
+// the passes repeat until the row is covered). The k dot products are
+// reduced across the wavefront.
 template <typename T, int CPL, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ dout, const T *__restrict__ y,
                                                           const float *__restrict__ tw,
@@ -149,6 +152,71 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ 
       const float d = wave_sum(dot[j]);
       if (lane == 0) dtw[t * k + j] = d;
     }
+  }
+}
+
+// B1 for wide rows (at least 256 chunks): one workgroup of NT threads per
+// token, thread i taking chunks i, i + NT, ...: a token's rows are then read
+// and written as NT-chunk runs by the whole workgroup, which streams faster
+// than a wavefront walking the row (measured 1% faster at d = 2048, 7% at
+// d = 4096). The k dot products are reduced in each wavefront, then across
+// the wavefronts in a fixed order.
+template <typename T, int NT, int KMAX>
+__global__ __launch_bounds__(NT) void combine_bwd_wide_kernel(const T *__restrict__ dout, const T *__restrict__ y,
+                                                              const float *__restrict__ tw,
+                                                              const int32_t *__restrict__ ros, T *__restrict__ dy,
+                                                              float *__restrict__ dtw, int64_t ntok, int nc, int k) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int NW = NT / 64;
+  __shared__ float part[NW][KMAX];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t t = blockIdx.x;
+  const int64_t ld = (int64_t)nc * V;
+  const int64_t nrows = ntok * k;
+  int64_t row[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    row[j] = j < k ? ros[t * k + j] : -1;
+    w[j] = j < k ? tw[t * k + j] : 0.f;
+  }
+  float dot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) dot[j] = 0.f;
+  for (int c = tid; c < nc; c += NT) {
+    float gv[V];
+    Elem<T>::unpack(ld16_nt(dout + t * ld + (int64_t)c * V), gv);
+    u32x4_t raw[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const bool ok = j < k && (uint64_t)row[j] < (uint64_t)nrows;
+      raw[j] = ok ? ld16_nt(y + row[j] * ld + (int64_t)c * V) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k && (uint64_t)row[j] < (uint64_t)nrows) {
+        float v[V], o[V];
+        Elem<T>::unpack(raw[j], v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          dot[j] = fmaf(gv[i], v[i], dot[j]);
+          o[i] = w[j] * gv[i];
+        }
+        st16(dy + row[j] * ld + (int64_t)c * V, Elem<T>::pack(o));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const float d = wave_sum(dot[j]);
+    if (lane == 0) part[wv][j] = d;
+  }
+  __syncthreads();
+  if (tid < k) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) s += part[q][tid];
+    dtw[t * k + tid] = s;
   }
 }
 
@@ -259,13 +327,20 @@ static void combine_bwd_c(const T *dout, const T *y, const float *tw, const int3
 template <typename T>
 static void combine_bwd_dispatch(const T *dout, const T *y, const float *tw, const int32_t *ros, T *dy,
                                  float *dtw, int64_t ntok, int nc, int k, hipStream_t s) {
+  if (nc >= 256) {  // one workgroup per token
+    with_kmax(k, [&](auto km) {
+      constexpr int KM = decltype(km)::value;
+      if (nc >= 512)
+        combine_bwd_wide_kernel<T, 512, KM><<<dim3((unsigned)ntok), 512, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
+      else
+        combine_bwd_wide_kernel<T, 256, KM><<<dim3((unsigned)ntok), 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
+    });
+    return;
+  }
   const int cpl = (nc + 63) / 64;
   if (cpl <= 1) combine_bwd_c<T, 1>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
   else if (cpl <= 2) combine_bwd_c<T, 2>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
-  else if (cpl <= 4) combine_bwd_c<T, 4>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
-  else if (cpl <= 8) combine_bwd_c<T, 8>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
-  else if (cpl <= 16) combine_bwd_c<T, 16>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
-  else combine_bwd_c<T, 32>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);  // several passes past 2048 chunks
+  else combine_bwd_c<T, 4>(dout, y, tw, ros, dy, dtw, ntok, nc, k, s);
 }
 
 hipError_t launch_combine_bwd(const void *dout, const void *y, const float *topk_w, const int32_t *row_of_slot,
