@@ -59,6 +59,7 @@ GEMM_KERNELS = {
     "gg_gateup_wgrad": 4, "gg_gateup_recompute": 4,
 }
 MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
+ROUTE_TOKENS = 64  # tokens per workgroup of the route pass (its histograms are [T/64, E] int32)
 
 # HBM-side bytes per launch measured with rocprofv3 FETCH_SIZE and WRITE_SIZE
 # passes (each scaled by what the counter reads for a plain 1 GiB device copy:
@@ -364,7 +365,7 @@ def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
             # theta, grad, m, v read; theta, m, v, bf16 copy, zeroed grad written
             by = 3 * w.E * w.F * w.d * (28 + (2 if w.dtype == BF16 else 0) + 4)
         elif route_bytes(name, 1, w.E, w.k, 1) is not None:
-            by = sum(route_bytes(name, mb["T"], w.E, w.k, -(-mb["T"] // 256), args.renorm) for mb in mbs if mb["T"])
+            by = sum(route_bytes(name, mb["T"], w.E, w.k, -(-mb["T"] // ROUTE_TOKENS), args.renorm) for mb in mbs if mb["T"])
         if by is not None:
             gbps = by / (ms / steps * 1e-3) / 1e9
             entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
@@ -380,7 +381,7 @@ def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
     mem_by = sum(mem_bytes(n, mb["T"], w.d, w.k, s, router) for n in mem_names for mb in mbs)
     route_names = [n for n in kernels if route_bytes(n, 1, w.E, w.k, 1) is not None]
     route_ms = sum(kernels[n]["total_ms_per_step"] for n in route_names)
-    route_by = sum(route_bytes(n, mb["T"], w.E, w.k, -(-mb["T"] // 256), args.renorm)
+    route_by = sum(route_bytes(n, mb["T"], w.E, w.k, -(-mb["T"] // ROUTE_TOKENS), args.renorm)
                    for n in route_names for mb in mbs if mb["T"])
     # executed GEMM FLOPs (the recompute product included) over GEMM time
     gemm_tf = gemm_fl / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0

@@ -63,7 +63,7 @@ def test_cpu_baseline_object():
 
 def test_route_bytes():
     T, E, k = 32768, 32, 8
-    nblk = T // 256
+    nblk = T // bench.ROUTE_TOKENS
     assert bench.route_bytes("route_topk", T, E, k, nblk) == T * (4 * E + 12 * k) + 4 * nblk * E
     assert bench.route_bytes("route_bwd", T, E, k, nblk) == T * (8 * E + 12 * k)
     assert bench.route_bytes("route_bwd", T, E, k, nblk, renorm=True) == T * (4 * E + 12 * k)

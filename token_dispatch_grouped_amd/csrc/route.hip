@@ -106,7 +106,8 @@ MOE_DEVICE void for_row(const float *__restrict__ row, int E, F f) {
 // stable rank of each (token, slot) among the workgroup's slots of the same
 // expert, and the workgroup's expert histogram.
 //
-// One thread per token, 256 tokens per workgroup (4 wavefronts). Top-k keeps
+// One thread per token, kRouteTokensPerBlock tokens per workgroup (one
+// wavefront: 512 workgroups at 32k tokens, so every CU gets work). Top-k keeps
 // a descending list of 64-bit composite keys (logit key, then inverted id so
 // that the lower id wins a tie). A token selects an expert at most once, so
 // the rank of slot (t, j) among the workgroup's slots of expert e is the
@@ -117,20 +118,23 @@ MOE_DEVICE void for_row(const float *__restrict__ row, int E, F f) {
 // that of the own mask below the lane. No atomic decides any order.
 // ---------------------------------------------------------------------------
 template <int KMAX>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
+__global__ __launch_bounds__(kRouteTokensPerBlock) void route_topk_kernel(const float *__restrict__ logits,
                                                          int32_t *__restrict__ topk_idx,
                                                          float *__restrict__ topk_w,
                                                          int32_t *__restrict__ local_rank,
                                                          int32_t *__restrict__ blk_cnt, int64_t ntok, int E,
                                                          int k, int renorm) {
-  __shared__ unsigned long long s_mask[4][256];
+  constexpr int NT = kRouteTokensPerBlock;
+  constexpr int NW = NT / 64;
+  static_assert(NW * 64 == NT, "whole wavefronts per workgroup");
+  __shared__ unsigned long long s_mask[NW][256];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  const int64_t t = (int64_t)blockIdx.x * NT + tid;
   const bool valid = t < ntok;
 
-  for (int i = tid; i < 4 * 256; i += 256) (&s_mask[0][0])[i] = 0ull;
+  for (int i = tid; i < NW * 256; i += NT) (&s_mask[0][0])[i] = 0ull;
 
   uint64_t list[KMAX];
 #pragma unroll
@@ -198,9 +202,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
       }
     }
   }
-  for (int e = tid; e < E; e += 256)
-    blk_cnt[(int64_t)blockIdx.x * E + e] = __popcll(s_mask[0][e]) + __popcll(s_mask[1][e]) +
-                                           __popcll(s_mask[2][e]) + __popcll(s_mask[3][e]);
+  for (int e = tid; e < E; e += NT) {
+    int c = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) c += __popcll(s_mask[w2][e]);
+    blk_cnt[(int64_t)blockIdx.x * E + e] = c;
+  }
 }
 
 // Block-wide exclusive scan of one int per thread (256 threads); returns the
@@ -275,14 +282,16 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const int32_t *__restri
 // ---------------------------------------------------------------------------
 // B2: dlogits from dtopk_w. One thread per token.
 // ---------------------------------------------------------------------------
+constexpr int kRouteBwdThreads = 64;  // one wavefront per workgroup: 512 workgroups at 32k tokens
+
 template <int KMAX>
-__global__ __launch_bounds__(256) void route_bwd_kernel(const float *__restrict__ dtopk_w,
+__global__ __launch_bounds__(kRouteBwdThreads) void route_bwd_kernel(const float *__restrict__ dtopk_w,
                                                         const float *__restrict__ logits,
                                                         const int32_t *__restrict__ topk_idx,
                                                         const float *__restrict__ topk_w,
                                                         float *__restrict__ dlogits, int64_t ntok, int E, int k,
                                                         int renorm, int accumulate) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kRouteBwdThreads + threadIdx.x;
   if (t >= ntok) return;
   const float *row = logits + t * E;
   float *drow = dlogits + t * E;
@@ -419,7 +428,8 @@ template <int KMAX>
 static void launch_topk_k(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *rank, int32_t *blk_cnt,
                           int64_t T, int E, int k, bool renorm, hipStream_t s) {
   dim3 grid((unsigned)route_blocks(T));
-  route_topk_kernel<KMAX><<<grid, 256, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, renorm ? 1 : 0);
+  route_topk_kernel<KMAX><<<grid, kRouteTokensPerBlock, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k,
+                                                                 renorm ? 1 : 0);
 }
 
 // Scratch of the allocation-free routing entry point (moe_route_noalloc):
@@ -488,16 +498,16 @@ hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int
                             const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
                             bool accumulate, hipStream_t s) {
   LaunchScope scope("route_bwd", s);
-  dim3 grid((unsigned)((T + 255) / 256));
+  dim3 grid((unsigned)((T + kRouteBwdThreads - 1) / kRouteBwdThreads));
   const int r = renorm ? 1 : 0, a = accumulate ? 1 : 0;
   if (k <= 2)
-    route_bwd_kernel<2><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    route_bwd_kernel<2><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   else if (k <= 4)
-    route_bwd_kernel<4><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    route_bwd_kernel<4><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   else if (k <= 8)
-    route_bwd_kernel<8><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    route_bwd_kernel<8><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   else
-    route_bwd_kernel<16><<<grid, 256, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    route_bwd_kernel<16><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
   return hipGetLastError();
 }
 

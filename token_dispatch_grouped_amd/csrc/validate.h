@@ -12,7 +12,7 @@
 namespace moe {
 
 // Tile sizes the launchers use; validation checks that grids fit.
-constexpr int kRouteTokens = 256;       // tokens per top-k workgroup
+constexpr int kRouteTokens = 64;        // tokens per top-k workgroup (one wavefront)
 constexpr int kRouterChunksMax = 32;    // router weight-gradient partial sums
 constexpr int kGemmBM = 256;            // bf16 grouped GEMM rows per tile
 constexpr int kGemmBN = 256;            // bf16 grouped GEMM columns per tile
@@ -21,7 +21,8 @@ constexpr int kGemmF32Tile = 16;        // fp32 grouped GEMM tile edge
 constexpr int kAuxMaxBlocks = 1024;     // partial rows of the auxiliary-loss pass
 // Static per-GPU scratch of moe_route_noalloc: the per-workgroup expert
 // histograms of the route pass, ceil(T / kRouteTokens) * E int32.
-constexpr size_t kRouteScratchBytes = (size_t)4 << 20;
+constexpr size_t kRouteScratchBytes = (size_t)16 << 20;
+constexpr int kEpMaxRanks = 8;          // expert-parallel ranks of the exchange stand-in (one node)
 
 struct WorkspaceLayout {
   size_t route_blk_cnt;   // bytes of the per-workgroup expert histograms
@@ -69,6 +70,11 @@ moe_status validate_adamw(const moe_adamw_config *cfg, int64_t n, std::string *w
 
 // Auxiliary-loss coefficients and flags (see moe_aux_loss).
 moe_status validate_aux(const moe_aux_config *cfg, std::string *why);
+
+// Expert-parallel exchange sizes: 1 <= ep <= kEpMaxRanks, e_local >= 1,
+// ep*e_local <= 256; d a positive multiple of 64 (<= 65536) and dtype valid
+// when d > 0 is given; capacities >= 0 and below 2^31 rows.
+moe_status validate_ep(int32_t ep, int32_t e_local, int32_t d, int32_t dtype, int64_t rows_cap, std::string *why);
 
 // Workspace check: NULL or short -> MOE_ERR_WORKSPACE (a zero requirement
 // accepts anything).
