@@ -151,9 +151,9 @@ moe_status moe_route(const moe_shape *shape, const void *x, const void *w_router
  * moe_route without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation). Arguments, results and errors are those of moe_route;
- * the per-workgroup histograms go to a static scratch array of 4 MiB per GPU
+ * the per-workgroup histograms go to a static scratch array of 16 MiB per GPU
  * instead (held by each GPU the library runs on until the process ends), so
- * ceil(T / 256) * E * 4 bytes must fit in it: T up to 1,048,576 tokens at
+ * ceil(T / 64) * E * 4 bytes must fit in it: T up to 1,048,576 tokens at
  * E = 256, 8,388,608 at E = 32. Larger shapes return MOE_ERR_UNSUPPORTED
  * before anything is launched. The call allocates no device memory. Every
  * call on one GPU shares that GPU's scratch: calls that overlap in time on
@@ -364,6 +364,91 @@ typedef struct moe_adamw_config {
 
 moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, float *grad,
                           float *exp_avg, float *exp_avg_sq, void *param_bf16, moe_stream_t stream);
+
+/*
+ * Expert parallelism: the token exchange between EP ranks around the grouped
+ * FFN, for EP combined with data parallelism where ranks hold different token
+ * counts, uneven work or none, and the runtime (not the caller) coordinates
+ * expert communication, its order and its buffer capacities (Support combined
+ * expert and data parallelism in TrainerRank, Desired behavior; an EP=2 run on
+ * unequal batches with an empty-work case: same page, Acceptance).
+ *
+ * Global expert g = r*E_local + e is local expert e of rank r (EP ranks,
+ * E = EP*E_local experts in all). A source rank routes its tokens over all E
+ * experts with moe_route and dispatches them with moe_permute: its x_perm is
+ * then one contiguous segment per destination rank, ordered by local expert,
+ * then source token. A destination numbers the rows it receives
+ * source-major (all of source 0's segment, then source 1's, ...) and runs
+ * the grouped FFN on them regrouped by local expert, then source, then their
+ * order in the segment. Every count stays on the device; the host passes
+ * capacities only. 1 <= EP <= MOE_EP_MAX_RANKS, EP*E_local <= 256.
+ */
+enum { MOE_EP_MAX_RANKS = 8 };
+
+/*
+ * Send plan of one source rank (shape->E = EP*E_local global experts), from
+ * the counts [E] and offsets [E+1] moe_route wrote:
+ *   send_counts[r*E_local + e] = counts[r*E_local + e]    [EP*E_local] int32
+ *   send_offsets[r] = offsets[r*E_local], send_offsets[EP] = offsets[E]
+ *                                                          [EP+1] int32
+ * (rows [send_offsets[r], send_offsets[r+1]) of x_perm go to rank r). With
+ * T == 0 both tables are written as zeros and counts/offsets may be NULL: a
+ * rank with no work still takes part in the counts exchange. This is the
+ * second exception to "T == 0 writes nothing".
+ * Errors: ep outside [1, MOE_EP_MAX_RANKS] or not dividing E ->
+ * MOE_ERR_UNSUPPORTED; plus the shape and pointer rules of the other calls.
+ */
+moe_status moe_ep_send_plan(const moe_shape *shape, int32_t ep, const int32_t *counts, const int32_t *offsets,
+                            int32_t *send_counts, int32_t *send_offsets, moe_stream_t stream);
+
+/*
+ * Receive plan of one destination rank from recv_counts [EP*E_local] int32
+ * (entry s*E_local + e: rows of local expert e that source s sends):
+ *   local_counts[e] = sum_s recv_counts[s*E_local + e]        [E_local]
+ *   local_offsets = exclusive scan of local_counts             [E_local+1]
+ *   recv_offsets[s] = first received row of source s           [EP+1]
+ *   regroup_row[i] = grouped row of received row i, for i < recv_offsets[EP]
+ *                                                              [rows_cap]
+ * rows_cap is the capacity of the receive and grouped buffers (rows the
+ * host sized them for, e.g. EP * T_max * k); entries of regroup_row at or past
+ * the received total are not written. local_offsets is the `offsets` of the
+ * grouped FFN calls on the grouped rows (shape T = rows_cap, k = 1,
+ * E = E_local).
+ */
+moe_status moe_ep_recv_plan(int32_t ep, int32_t e_local, int64_t rows_cap, const int32_t *recv_counts,
+                            int32_t *local_counts, int32_t *local_offsets, int32_t *recv_offsets,
+                            int32_t *regroup_row, moe_stream_t stream);
+
+/*
+ * Regroup of the received rows i < recv_offsets[EP] (d columns of dtype):
+ *   reverse == 0: dst[regroup_row[i]] = src[i]   (received -> grouped)
+ *   reverse != 0: dst[i] = src[regroup_row[i]]   (grouped -> received)
+ * src and dst hold rows_cap rows and do not overlap.
+ */
+moe_status moe_ep_regroup(int32_t d, int32_t dtype, int64_t rows_cap, int32_t ep, const int32_t *recv_offsets,
+                          const int32_t *regroup_row, const void *src, void *dst, int32_t reverse,
+                          moe_stream_t stream);
+
+/*
+ * One-GPU stand-ins for the two exchanges between the EP ranks, for EP
+ * ranks simulated on one device (the multi-GPU path replaces them with an
+ * all-to-all of the counts tables and an all-to-allv of the rows). Arrays of
+ * EP device pointers are host arrays indexed by rank.
+ *
+ * Counts: recv_counts[r][s*E_local + e] = send_counts[s][r*E_local + e].
+ *
+ * Rows (reverse == 0): for every source s and destination r, rows
+ * [send_offsets[s][r], send_offsets[s][r+1]) of send_bufs[s] go to rows
+ * recv_offsets[r][s] .. of recv_bufs[r]; reverse != 0 copies the same rows
+ * back into send_bufs. send_caps[s] / recv_caps[r]: rows each buffer holds
+ * (a source with T = 0 has capacity 0 and sends nothing). d columns of dtype.
+ */
+moe_status moe_ep_exchange_counts_loopback(int32_t ep, int32_t e_local, const int32_t *const *send_counts,
+                                           int32_t *const *recv_counts, moe_stream_t stream);
+moe_status moe_ep_exchange_loopback(int32_t ep, int32_t d, int32_t dtype, void *const *send_bufs,
+                                    const int64_t *send_caps, const int32_t *const *send_offsets,
+                                    void *const *recv_bufs, const int64_t *recv_caps,
+                                    const int32_t *const *recv_offsets, int32_t reverse, moe_stream_t stream);
 
 /* Static English text for a status code. */
 const char *moe_status_string(moe_status status);

@@ -59,6 +59,41 @@ def test_peak_probe_argument_rules():
         assert ei.value.status == st
 
 
+def test_ep_argument_rules():
+    """The expert-parallel calls validate before any launch."""
+    s = shape(T=64, E=8, k=2)
+    with pytest.raises(moe.MoeError) as ei:   # ep does not divide E
+        moe.moe_ep_send_plan(s, 3, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:   # more ranks than the stand-in holds
+        moe.moe_ep_send_plan(shape(T=64, E=16, k=2), 16, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:   # counts needed when T > 0
+        moe.moe_ep_send_plan(s, 2, None, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "counts" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:   # ep * e_local > 256
+        moe.moe_ep_recv_plan(4, 65, 100, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_ep_recv_plan(2, 4, -1, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(moe.MoeError) as ei:   # overlapping regroup buffers
+        moe.moe_ep_regroup(64, L.MOE_DTYPE_BF16, 100, 2, FAKE, FAKE, FAKE, FAKE + 256, stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "overlap" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:   # d not a multiple of 64
+        moe.moe_ep_regroup(96, L.MOE_DTYPE_BF16, 100, 2, FAKE, FAKE, FAKE, FAKE << 4, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:   # a NULL receive buffer with rows to receive
+        moe.moe_ep_exchange_loopback(2, 64, L.MOE_DTYPE_BF16, [FAKE, FAKE], [10, 10], [FAKE, FAKE], [FAKE, None],
+                                     [20, 20], [FAKE, FAKE], stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "recv_bufs" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_ep_exchange_counts_loopback(2, 4, [FAKE, None], [FAKE, FAKE], stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    # a zero-capacity regroup is a no-op that accepts NULL buffers
+    moe.moe_ep_regroup(64, L.MOE_DTYPE_BF16, 0, 2, None, None, None, None, stream=0)
+
+
 def test_version_and_status_strings():
     assert "gfx950" in moe.moe_version()
     assert moe.moe_status_string(0) == "ok"
@@ -101,13 +136,13 @@ def test_empty_microbatch_is_a_noop_with_nulls():
 
 def test_route_noalloc_argument_rules():
     """The allocation-free route validates like moe_route and rejects, before
-    any launch, shapes whose histograms exceed its 4 MiB static scratch."""
+    any launch, shapes whose histograms exceed its 16 MiB static scratch."""
     moe.moe_route_noalloc(shape(T=0), None, None, None, None, None, None, None, None, None, None, stream=0)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_route_noalloc(shape(T=300), None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "src_of_row" in str(ei.value)
-    # ceil(T/256) * E * 4 bytes: 4097 workgroups of 256 experts is one past the 4 MiB
-    big = shape(T=4097 * 256, E=256, k=8)
+    # ceil(T/64) * E * 4 bytes: 16385 workgroups of 256 experts is one past the 16 MiB
+    big = shape(T=16384 * 64 + 1, E=256, k=8)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_route_noalloc(big, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.status == L.MOE_ERR_UNSUPPORTED and "static scratch" in str(ei.value)

@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     MOE_FLAG_ACCUMULATE_DLOGITS, MOE_AUX_ACCUMULATE, MOE_METRIC_IMBALANCE, MOE_METRIC_EMPTY_EXPERTS,
     MOE_METRIC_COUNT_CV, MOE_METRIC_ENTROPY, MOE_METRIC_MAX_PROB, MOE_METRIC_SCALARS, make_aux_config,
     moe_aux_config, moe_aux_loss, moe_peak_mfma, moe_peak_mfma_size, moe_peak_copy,
+    MOE_EP_MAX_RANKS, moe_ep_send_plan, moe_ep_recv_plan, moe_ep_regroup, moe_ep_exchange_counts_loopback,
+    moe_ep_exchange_loopback,
 )
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "load", "make_shape",

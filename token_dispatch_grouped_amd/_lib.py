@@ -80,6 +80,13 @@ _SIGNATURES = {
     "moe_profiler_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
     "moe_version": (ctypes.c_char_p, []),
+    "moe_ep_send_plan": (ctypes.c_int, [_S, ctypes.c_int32, _P, _P, _P, _P, _P]),
+    "moe_ep_recv_plan": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
+    "moe_ep_regroup": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P,
+                                      ctypes.c_int32, _P]),
+    "moe_ep_exchange_counts_loopback": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "moe_ep_exchange_loopback": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                                ctypes.c_int32, _P]),
     # include/moe_peak.h
     "moe_peak_mfma": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _P]),
     "moe_peak_mfma_size": (ctypes.c_int64, []),
@@ -237,6 +244,52 @@ def moe_adamw_step(cfg, n, param, grad, exp_avg, exp_avg_sq, param_bf16=None, st
     lib = load()
     _check(lib.moe_adamw_step(ctypes.byref(cfg), int(n), ptr(param), ptr(grad), ptr(exp_avg), ptr(exp_avg_sq),
                               ptr(param_bf16), _stream(stream)), "moe_adamw_step")
+
+
+MOE_EP_MAX_RANKS = 8
+
+
+def _ptr_array(items):
+    """Host array of device pointers (None -> NULL) for the per-rank arguments."""
+    arr = (ctypes.c_void_p * len(items))(*[ptr(t) for t in items])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def _i64_array(vals):
+    arr = (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def moe_ep_send_plan(shape, ep, counts, offsets, send_counts, send_offsets, stream=None):
+    _check(load().moe_ep_send_plan(ctypes.byref(shape), int(ep), ptr(counts), ptr(offsets), ptr(send_counts),
+                                   ptr(send_offsets), _stream(stream)), "moe_ep_send_plan")
+
+
+def moe_ep_recv_plan(ep, e_local, rows_cap, recv_counts, local_counts, local_offsets, recv_offsets, regroup_row,
+                     stream=None):
+    _check(load().moe_ep_recv_plan(int(ep), int(e_local), int(rows_cap), ptr(recv_counts), ptr(local_counts),
+                                   ptr(local_offsets), ptr(recv_offsets), ptr(regroup_row), _stream(stream)),
+           "moe_ep_recv_plan")
+
+
+def moe_ep_regroup(d, dtype, rows_cap, ep, recv_offsets, regroup_row, src, dst, reverse=False, stream=None):
+    _check(load().moe_ep_regroup(int(d), int(dtype), int(rows_cap), int(ep), ptr(recv_offsets), ptr(regroup_row),
+                                 ptr(src), ptr(dst), 1 if reverse else 0, _stream(stream)), "moe_ep_regroup")
+
+
+def moe_ep_exchange_counts_loopback(ep, e_local, send_counts, recv_counts, stream=None):
+    sp, _a = _ptr_array(send_counts)
+    rp, _b = _ptr_array(recv_counts)
+    _check(load().moe_ep_exchange_counts_loopback(int(ep), int(e_local), sp, rp, _stream(stream)),
+           "moe_ep_exchange_counts_loopback")
+
+
+def moe_ep_exchange_loopback(ep, d, dtype, send_bufs, send_caps, send_offsets, recv_bufs, recv_caps, recv_offsets,
+                             reverse=False, stream=None):
+    a = [_ptr_array(send_bufs), _i64_array(send_caps), _ptr_array(send_offsets), _ptr_array(recv_bufs),
+         _i64_array(recv_caps), _ptr_array(recv_offsets)]
+    _check(load().moe_ep_exchange_loopback(int(ep), int(d), int(dtype), *[x[0] for x in a], 1 if reverse else 0,
+                                           _stream(stream)), "moe_ep_exchange_loopback")
 
 
 def moe_peak_mfma_size() -> int:

@@ -110,6 +110,26 @@ hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *lo
                            float *partial, int64_t T, int E, int k, float alpha, float beta, bool accumulate,
                            hipStream_t s);
 
+// ----- expert-parallel exchange (ep.hip) -----
+struct EpPtrs {
+  void *p[kEpMaxRanks];
+};
+struct EpCaps {
+  int64_t n[kEpMaxRanks];
+};
+hipError_t launch_ep_send_plan(const int32_t *counts, const int32_t *offsets, int32_t *send_counts,
+                               int32_t *send_offsets, int ep, int e_local, bool empty, hipStream_t s);
+hipError_t launch_ep_recv_plan(const int32_t *recv_counts, int32_t *local_counts, int32_t *local_offsets,
+                               int32_t *recv_offsets, int32_t *regroup_row, int64_t rows_cap, int ep, int e_local,
+                               hipStream_t s);
+hipError_t launch_ep_regroup(const void *src, void *dst, const int32_t *regroup_row, const int32_t *total,
+                             int64_t rows_cap, int d, bool bf16, bool reverse, hipStream_t s);
+hipError_t launch_ep_exchange_counts(const EpPtrs &send_counts, const EpPtrs &recv_counts, int ep, int e_local,
+                                     hipStream_t s);
+hipError_t launch_ep_exchange_rows(void *src, const int32_t *send_off, int64_t src_cap, const EpPtrs &dst,
+                                   const EpPtrs &recv_off, const EpCaps &dst_cap, int source, int ep, int d,
+                                   bool bf16, bool reverse, hipStream_t s);
+
 // Attainable-peak probes (peak.hip): a bf16 MFMA loop on `cus` compute
 // units and a plain device copy.
 int peak_mfma_threads(int cus);

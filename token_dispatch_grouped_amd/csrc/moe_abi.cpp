@@ -494,6 +494,126 @@ moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, 
   return hip_status(launch_adamw(a, as_stream(stream)), "adamw_step");
 }
 
+moe_status moe_ep_send_plan(const moe_shape *shape, int32_t ep, const int32_t *counts, const int32_t *offsets,
+                            int32_t *send_counts, int32_t *send_offsets, moe_stream_t stream) {
+  moe::AbiRange range("moe_ep_send_plan");
+  std::string why;
+  moe_status st = validate_shape(shape, &why);
+  if (st != MOE_OK) return report(st, why);
+  const moe_shape &s = *shape;
+  if (ep < 1 || ep > kEpMaxRanks || s.E % ep != 0)
+    return report(MOE_ERR_UNSUPPORTED, "moe_ep_send_plan: ep outside [1, MOE_EP_MAX_RANKS] or not dividing E");
+  const bool empty = s.T == 0;
+  const PtrArg args[] = {{"counts", counts, !empty, false},
+                         {"offsets", offsets, !empty, false},
+                         {"send_counts", send_counts, true, false},
+                         {"send_offsets", send_offsets, true, false}};
+  st = validate_ptrs(args, 4, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(launch_ep_send_plan(counts, offsets, send_counts, send_offsets, ep, s.E / ep, empty,
+                                        as_stream(stream)),
+                    "ep_send_plan");
+}
+
+moe_status moe_ep_recv_plan(int32_t ep, int32_t e_local, int64_t rows_cap, const int32_t *recv_counts,
+                            int32_t *local_counts, int32_t *local_offsets, int32_t *recv_offsets,
+                            int32_t *regroup_row, moe_stream_t stream) {
+  moe::AbiRange range("moe_ep_recv_plan");
+  std::string why;
+  moe_status st = validate_ep(ep, e_local, 0, 0, rows_cap, &why);
+  if (st != MOE_OK) return report(st, why);
+  const PtrArg args[] = {{"recv_counts", recv_counts, true, false},
+                         {"local_counts", local_counts, true, false},
+                         {"local_offsets", local_offsets, true, false},
+                         {"recv_offsets", recv_offsets, true, false},
+                         {"regroup_row", regroup_row, rows_cap > 0, false}};
+  st = validate_ptrs(args, 5, &why);
+  if (st != MOE_OK) return report(st, why);
+  return hip_status(launch_ep_recv_plan(recv_counts, local_counts, local_offsets, recv_offsets, regroup_row, rows_cap,
+                                        ep, e_local, as_stream(stream)),
+                    "ep_recv_plan");
+}
+
+moe_status moe_ep_regroup(int32_t d, int32_t dtype, int64_t rows_cap, int32_t ep, const int32_t *recv_offsets,
+                          const int32_t *regroup_row, const void *src, void *dst, int32_t reverse,
+                          moe_stream_t stream) {
+  moe::AbiRange range("moe_ep_regroup");
+  std::string why;
+  moe_status st = validate_ep(ep, 1, d, dtype, rows_cap, &why);
+  if (st != MOE_OK) return report(st, why);
+  if (d == 0) return report(MOE_ERR_INVALID_ARGUMENT, "moe_ep_regroup: d must be positive");
+  if (rows_cap == 0) return MOE_OK;
+  const PtrArg args[] = {{"recv_offsets", recv_offsets, true, false},
+                         {"regroup_row", regroup_row, true, false},
+                         {"src", src, true, false},
+                         {"dst", dst, true, false}};
+  st = validate_ptrs(args, 4, &why);
+  if (st != MOE_OK) return report(st, why);
+  const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const char *a = static_cast<const char *>(src), *b = static_cast<const char *>(dst);
+  const size_t bytes = (size_t)rows_cap * (size_t)d * es;
+  if (a < b + bytes && b < a + bytes) return report(MOE_ERR_INVALID_ARGUMENT, "moe_ep_regroup: src and dst overlap");
+  return hip_status(launch_ep_regroup(src, dst, regroup_row, recv_offsets + ep, rows_cap, d, dtype == MOE_DTYPE_BF16,
+                                      reverse != 0, as_stream(stream)),
+                    "ep_regroup");
+}
+
+moe_status moe_ep_exchange_counts_loopback(int32_t ep, int32_t e_local, const int32_t *const *send_counts,
+                                           int32_t *const *recv_counts, moe_stream_t stream) {
+  moe::AbiRange range("moe_ep_exchange_counts_loopback");
+  std::string why;
+  moe_status st = validate_ep(ep, e_local, 0, 0, 0, &why);
+  if (st != MOE_OK) return report(st, why);
+  if (!send_counts || !recv_counts) return report(MOE_ERR_INVALID_ARGUMENT, "pointer arrays are NULL");
+  EpPtrs sp{}, rp{};
+  for (int r = 0; r < ep; ++r) {
+    const PtrArg args[] = {{"send_counts[r]", send_counts[r], true, false},
+                           {"recv_counts[r]", recv_counts[r], true, false}};
+    st = validate_ptrs(args, 2, &why);
+    if (st != MOE_OK) return report(st, why);
+    sp.p[r] = const_cast<int32_t *>(send_counts[r]);
+    rp.p[r] = recv_counts[r];
+  }
+  return hip_status(launch_ep_exchange_counts(sp, rp, ep, e_local, as_stream(stream)), "ep_exchange_counts");
+}
+
+moe_status moe_ep_exchange_loopback(int32_t ep, int32_t d, int32_t dtype, void *const *send_bufs,
+                                    const int64_t *send_caps, const int32_t *const *send_offsets,
+                                    void *const *recv_bufs, const int64_t *recv_caps,
+                                    const int32_t *const *recv_offsets, int32_t reverse, moe_stream_t stream) {
+  moe::AbiRange range("moe_ep_exchange_loopback");
+  std::string why;
+  moe_status st = validate_ep(ep, 1, d, dtype, 0, &why);
+  if (st != MOE_OK) return report(st, why);
+  if (d == 0) return report(MOE_ERR_INVALID_ARGUMENT, "moe_ep_exchange_loopback: d must be positive");
+  if (!send_bufs || !send_caps || !send_offsets || !recv_bufs || !recv_caps || !recv_offsets)
+    return report(MOE_ERR_INVALID_ARGUMENT, "pointer arrays are NULL");
+  EpPtrs dst{}, roff{};
+  EpCaps cap{};
+  for (int r = 0; r < ep; ++r) {
+    st = validate_ep(ep, 1, d, dtype, send_caps[r], &why);
+    if (st == MOE_OK) st = validate_ep(ep, 1, d, dtype, recv_caps[r], &why);
+    if (st != MOE_OK) return report(st, why);
+    const PtrArg args[] = {{"send_bufs[r]", send_bufs[r], send_caps[r] > 0, false},
+                           {"send_offsets[r]", send_offsets[r], true, false},
+                           {"recv_bufs[r]", recv_bufs[r], recv_caps[r] > 0, false},
+                           {"recv_offsets[r]", recv_offsets[r], true, false}};
+    st = validate_ptrs(args, 4, &why);
+    if (st != MOE_OK) return report(st, why);
+    dst.p[r] = recv_bufs[r];
+    roff.p[r] = const_cast<int32_t *>(recv_offsets[r]);
+    cap.n[r] = recv_caps[r];
+  }
+  hipStream_t hs = as_stream(stream);
+  for (int s = 0; s < ep; ++s) {
+    st = hip_status(launch_ep_exchange_rows(send_bufs[s], send_offsets[s], send_caps[s], dst, roff, cap, s, ep, d,
+                                            dtype == MOE_DTYPE_BF16, reverse != 0, hs),
+                    "ep_exchange_rows");
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
 static int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;

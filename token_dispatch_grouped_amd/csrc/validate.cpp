@@ -131,6 +131,21 @@ moe_status validate_adamw(const moe_adamw_config *c, int64_t n, std::string *why
   return MOE_OK;
 }
 
+moe_status validate_ep(int32_t ep, int32_t e_local, int32_t d, int32_t dtype, int64_t rows_cap, std::string *why) {
+  if (ep < 1 || ep > kEpMaxRanks) return fail(why, MOE_ERR_UNSUPPORTED, "ep outside [1, MOE_EP_MAX_RANKS]");
+  if (e_local < 1) return fail(why, MOE_ERR_INVALID_ARGUMENT, "e_local < 1");
+  if ((int64_t)ep * e_local > 256) return fail(why, MOE_ERR_UNSUPPORTED, "ep * e_local > 256");
+  if (d != 0) {
+    if (d < 0) return fail(why, MOE_ERR_INVALID_ARGUMENT, "d < 0");
+    if (d % 64 != 0 || d > 65536) return fail(why, MOE_ERR_UNSUPPORTED, "d must be a multiple of 64, at most 65536");
+    if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16)
+      return fail(why, MOE_ERR_UNSUPPORTED, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  }
+  if (rows_cap < 0) return fail(why, MOE_ERR_INVALID_ARGUMENT, "negative row capacity");
+  if (rows_cap >= ((int64_t)1 << 31)) return fail(why, MOE_ERR_UNSUPPORTED, "row capacity >= 2^31");
+  return MOE_OK;
+}
+
 moe_status validate_aux(const moe_aux_config *c, std::string *why) {
   if (!c) return fail(why, MOE_ERR_INVALID_ARGUMENT, "aux config is NULL");
   if (c->flags & ~(uint32_t)MOE_AUX_ACCUMULATE) return fail(why, MOE_ERR_UNSUPPORTED, "unknown aux flag bits");

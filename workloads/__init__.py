@@ -239,6 +239,36 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, object]:
     return {"weights": weights, "micro": micro}
 
 
+def make_ep_inputs(ep: int, Ts, d: int, e_local: int, k: int, F: int, dtype: str = BF16, seed: int = 0,
+                   routing: str = "normal", zipf_s: float = 1.2, n_empty: int = 0) -> Dict[str, object]:
+    """Inputs of EP ranks simulated together: weights of all ep * e_local
+    experts, and per source rank its tokens x [T_s, d], routing logits
+    [T_s, E] (N(0,1), or Zipf popularity over the global experts with n_empty
+    experts forced empty, the same popularity on every rank) and dout.
+    Draw order: weights, then per source x, logits noise, dout."""
+    E = ep * e_local
+    w = Workload(f"ep{ep}", seed, max(Ts) if len(Ts) else 0, d, E, k, F, dtype, routing, zipf_s=zipf_s,
+                 n_empty=n_empty)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    weights = make_weights(w, rng)
+    perm = rng.permutation(E) if routing == "zipf" else None
+    micro = []
+    for T in Ts:
+        x = store(_normal(rng, (T, d), 1.0), dtype)
+        if routing == "zipf":
+            empty, live = perm[:n_empty], perm[n_empty:]
+            pop = np.zeros(E)
+            pop[live] = np.arange(1, len(live) + 1, dtype=np.float64) ** (-zipf_s)
+            logp = np.full(E, -1e4)
+            logp[live] = np.log(pop[live] / pop.sum())
+            lg = (logp.astype(np.float32)[None, :] + rng.gumbel(size=(T, E)).astype(np.float32)).astype(np.float32)
+            lg[:, empty] = np.float32(-1e4)
+        else:
+            lg = _normal(rng, (T, E), 1.0)
+        micro.append({"x": x, "logits": np.ascontiguousarray(lg), "dout": store(_normal(rng, (T, d), 1.0), dtype)})
+    return {"weights": weights, "micro": micro}
+
+
 def tie_logits(T: int, E: int, seed: int, levels: int = 3) -> np.ndarray:
     """fp32 logits drawn from a handful of integer levels, so that most tokens
     hold ties (used to exercise the lowest-id tie-break)."""
@@ -257,6 +287,6 @@ def describe(w: Workload) -> str:
 
 __all__ = [
     "F32", "BF16", "Workload", "WORKLOADS", "small_workload", "make_inputs", "make_weights",
-    "make_microbatch", "tie_logits", "f32_to_bf16_bits", "bf16_bits_to_f32", "to_f64", "store",
+    "make_microbatch", "make_ep_inputs", "tie_logits", "f32_to_bf16_bits", "bf16_bits_to_f32", "to_f64", "store",
     "flops_per_routed_row", "describe",
 ]
