@@ -26,10 +26,12 @@ zeroed in the same pass) to every training step; its kernel is reported as
 ``adamw`` with 34 bytes per weight element.
 
 With the default workload (ep_share_32k) the line also carries
-``other_32k_workloads``: the empty-microbatch accumulation run and the d=4096
+``other_32k_workloads``: the empty-microbatch accumulation run, the d=4096
 uniform and Zipf shares, each timed the same way over ``--other-steps``
 steps (ms/step, layer TFLOP/s, grouped-GEMM % of peak, permute/combine GB/s,
-per-kernel times). ``attainable`` holds the rates the library's probes reach
+per-kernel times), and two expert-parallel ranks simulated on one GPU with
+uneven token counts (``ep2_loopback_32k``: 64 experts, 32 per rank, the
+exchanges as device copies; the exchange and regroup kernels in GB/s). ``attainable`` holds the rates the library's probes reach
 on this GPU (a bf16 MFMA loop from registers and a 1 GiB device copy); every
 GEMM and memory kernel is also reported as a percentage of those
 (``pct_attainable``). Routing kernels report GB/s on their algorithmic bytes
@@ -444,6 +446,113 @@ def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
 # the other 32k-token workloads, timed after the headline one in the default run
 OTHER_32K = ("microbatches_32k", "large_share_uniform", "large_share_zipf")
 
+# Expert-parallel ranks simulated on one GPU: two ranks of 32 local experts
+# (64 in all), the second rank holding half the tokens of the first (uneven
+# data-parallel inputs), Zipf(1.2) popularity over the 64 experts with 4 empty
+EP_LOOPBACK = dict(name="ep2_loopback_32k", ep=2, Ts=(32768, 16384), d=2048, e_local=32, k=8, F=1408, seed=7,
+                   zipf_s=1.2, n_empty=4)
+EP_ROW_KERNELS = ("ep_exchange_rows", "ep_return_rows", "ep_regroup", "ep_ungroup")  # the last two: unfused only
+
+
+def measure_ep(cfg, steps, warmup, attain=None):
+    """The EP loopback step (forward + backward of every simulated rank,
+    exchanges included), timed like measure(); GEMM and memory kernels summed
+    over the ranks."""
+    import numpy as np
+    import torch
+
+    import token_dispatch_grouped_amd as moe
+    from token_dispatch_grouped_amd.ep import EpLoopback
+    from workloads import make_ep_inputs
+
+    dev = torch.device("cuda:0")
+    ep, Ts, d, el, k, F = cfg["ep"], cfg["Ts"], cfg["d"], cfg["e_local"], cfg["k"], cfg["F"]
+    t_gen = time.perf_counter()
+    inp = make_ep_inputs(ep, Ts, d, el, k, F, "bf16", seed=cfg["seed"], routing="zipf", zipf_s=cfg["zipf_s"],
+                         n_empty=cfg["n_empty"])
+    t_gen = time.perf_counter() - t_gen
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    torch.cuda.reset_peak_memory_stats(dev)
+    lay = EpLoopback(ep, max(Ts), d, el, k, F, moe.MOE_DTYPE_BF16)
+    wgu, wdn = dev_t(inp["weights"]["w_gu"]), dev_t(inp["weights"]["w_down"])
+    xs = [dev_t(mb["x"]) for mb in inp["micro"]]
+    lgs = [dev_t(mb["logits"]) for mb in inp["micro"]]
+    douts = [dev_t(mb["dout"]) for mb in inp["micro"]]
+    dw_gu = torch.zeros(ep * el, 2 * F, d, dtype=torch.float32, device=dev)
+    dw_dn = torch.zeros(ep * el, d, F, dtype=torch.float32, device=dev)
+
+    def step():
+        lay.forward(Ts, xs, lgs, wgu, wdn)
+        lay.backward(douts, wgu, wdn, dw_gu, dw_dn)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(profile):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        moe.moe_profiler_reset()
+        moe.moe_profiler_enable(profile)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        moe.moe_profiler_enable(False)
+        return ev0.elapsed_time(ev1)
+
+    ms = timed(False) / steps
+    timed(True)
+    kern = moe.moe_profiler_read_all()
+    R = sum(T * k for T in Ts)
+    flops = 18.0 * R * d * F
+    kernels = {}
+    for name, (n, tot) in kern.items():
+        e = {"launches_per_step": n // steps, "total_ms_per_step": round(tot / steps, 4)}
+        if name in GEMM_KERNELS:
+            # summed over the destination ranks: each product's FLOPs over all rows
+            tf = GEMM_KERNELS[name] * R * d * F / (tot / steps * 1e-3) / 1e12
+            e.update(tflops=round(tf, 2), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
+        by = None
+        if name in MEM_KERNELS:
+            by = sum(mem_bytes(name, T, d, k, 2) for T in Ts)
+        elif name in EP_ROW_KERNELS:
+            # two calls per step (x and dy out, y and dx back); every row read and written once,
+            # the regroup also reads its row map
+            by = 2 * R * (2 * d * 2 + (4 if name in ("ep_regroup", "ep_ungroup") else 0))
+        if by is not None:
+            gbps = by / (tot / steps * 1e-3) / 1e9
+            e.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
+            if attain:
+                e["pct_attainable"] = round(100 * gbps / attain["copy_GBps"], 2)
+        kernels[name] = e
+    gemm_ms = sum(kernels[n]["total_ms_per_step"] for n in kernels if n in GEMM_KERNELS)
+    xch = [n for n in kernels if n in EP_ROW_KERNELS]
+    xch_ms = sum(kernels[n]["total_ms_per_step"] for n in xch)
+    xch_by = sum(2 * R * (2 * d * 2 + (4 if n in ("ep_regroup", "ep_ungroup") else 0)) for n in xch)
+    res = {"value": round(flops / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 4), "steps": steps,
+           "ep": ep, "T_per_rank": list(Ts), "d": d, "E_local": el, "E_total": ep * el, "k": k, "F": F,
+           "grouped_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
+           "exchange_regroup_GBps": round(xch_by / (xch_ms * 1e-3) / 1e9, 1) if xch_ms else None,
+           "exchange_regroup_ms_per_step": round(xch_ms, 4),
+           "device_memory_GB": round(torch.cuda.max_memory_allocated(dev) / 1e9, 2), "input_gen_s": round(t_gen, 2),
+           "kernels": kernels,
+           "note": "all ranks simulated on one GPU; the row and counts exchanges are device copies standing in for "
+                   "the all-to-all(v) between GPUs"}
+    if res["grouped_gemm_tflops"]:
+        res["grouped_gemm_pct_peak"] = round(100 * res["grouped_gemm_tflops"] / PEAK_BF16_TFLOPS, 2)
+    del lay, wgu, wdn, xs, lgs, douts, dw_gu, dw_dn
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
 
 def main():
     args = parse()
@@ -499,6 +608,8 @@ def main():
                                                                      "pct_peak")}
                             for n, e in r["kernels"].items()}
             others[name] = o
+        print(f"[bench] {EP_LOOPBACK['name']}", file=sys.stderr, flush=True)
+        others[EP_LOOPBACK["name"]] = measure_ep(EP_LOOPBACK, args.other_steps, min(args.warmup, 3), attain)
         line["other_32k_workloads"] = others
 
     if args.cpu_seconds > 0:

@@ -438,17 +438,21 @@ moe_status moe_ep_regroup(int32_t d, int32_t dtype, int64_t rows_cap, int32_t ep
  * Counts: recv_counts[r][s*E_local + e] = send_counts[s][r*E_local + e].
  *
  * Rows (reverse == 0): for every source s and destination r, rows
- * [send_offsets[s][r], send_offsets[s][r+1]) of send_bufs[s] go to rows
- * recv_offsets[r][s] .. of recv_bufs[r]; reverse != 0 copies the same rows
- * back into send_bufs. send_caps[s] / recv_caps[r]: rows each buffer holds
- * (a source with T = 0 has capacity 0 and sends nothing). d columns of dtype.
+ * [send_offsets[s][r], send_offsets[s][r+1]) of send_bufs[s] are received by
+ * r as rows recv_offsets[r][s] .. and land there in recv_bufs[r], or, if
+ * regroup_rows is non-NULL, straight at their grouped rows
+ * regroup_rows[r][received row] (the exchange and moe_ep_regroup in one
+ * copy). reverse != 0 copies the same rows back into send_bufs from the same
+ * places. send_caps[s] / recv_caps[r]: rows each buffer holds (a source with
+ * T = 0 has capacity 0 and sends nothing). d columns of dtype.
  */
 moe_status moe_ep_exchange_counts_loopback(int32_t ep, int32_t e_local, const int32_t *const *send_counts,
                                            int32_t *const *recv_counts, moe_stream_t stream);
 moe_status moe_ep_exchange_loopback(int32_t ep, int32_t d, int32_t dtype, void *const *send_bufs,
                                     const int64_t *send_caps, const int32_t *const *send_offsets,
                                     void *const *recv_bufs, const int64_t *recv_caps,
-                                    const int32_t *const *recv_offsets, int32_t reverse, moe_stream_t stream);
+                                    const int32_t *const *recv_offsets, const int32_t *const *regroup_rows,
+                                    int32_t reverse, moe_stream_t stream);
 
 /* Static English text for a status code. */
 const char *moe_status_string(moe_status status);

@@ -87,6 +87,10 @@ def test_ep_argument_rules():
         moe.moe_ep_exchange_loopback(2, 64, L.MOE_DTYPE_BF16, [FAKE, FAKE], [10, 10], [FAKE, FAKE], [FAKE, None],
                                      [20, 20], [FAKE, FAKE], stream=0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "recv_bufs" in str(ei.value)
+    with pytest.raises(moe.MoeError) as ei:   # a NULL regroup map for a destination with capacity
+        moe.moe_ep_exchange_loopback(2, 64, L.MOE_DTYPE_BF16, [FAKE, FAKE], [10, 10], [FAKE, FAKE], [FAKE, FAKE],
+                                     [20, 20], [FAKE, FAKE], regroup_rows=[FAKE, None], stream=0)
+    assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "regroup_rows" in str(ei.value)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_ep_exchange_counts_loopback(2, 4, [FAKE, None], [FAKE, FAKE], stream=0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT

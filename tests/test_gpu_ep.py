@@ -36,12 +36,12 @@ CASES = [
 ]
 
 
-def _run(ep, Ts, d, e_local, k, F, dtype, inp):
+def _run(ep, Ts, d, e_local, k, F, dtype, inp, fused=True):
     import torch
     import token_dispatch_grouped_amd as m
     from token_dispatch_grouped_amd.ep import EpLoopback
     mdt = m.MOE_DTYPE_BF16 if dtype == BF16 else m.MOE_DTYPE_F32
-    lay = EpLoopback(ep, max(max(Ts), 1), d, e_local, k, F, mdt)
+    lay = EpLoopback(ep, max(max(Ts), 1), d, e_local, k, F, mdt, fused=fused)
     W = inp["weights"]
     wgu, wdn = to_device(W["w_gu"], dtype), to_device(W["w_down"], dtype)
     xs = [to_device(mb["x"], dtype) for mb in inp["micro"]]
@@ -60,16 +60,22 @@ def _run(ep, Ts, d, e_local, k, F, dtype, inp):
     return lay, outs, fwd, [{k_: to_host64(v) for k_, v in g.items()} for g in grads], to_host64(dw_gu), to_host64(dw_dn)
 
 
-@pytest.mark.parametrize("name,ep,Ts,d,e_local,k,F,dtype,routing,n_empty", CASES, ids=[c[0] for c in CASES])
-def test_ep_loopback_matches_oracle(name, ep, Ts, d, e_local, k, F, dtype, routing, n_empty):
-    print(f"[ep] {name}: ep={ep} T={Ts} d={d} E_local={e_local} k={k} F={F} {dtype}", flush=True)
+# the unfused path (exchange in receive order, then moe_ep_regroup and back) on a few of the cases
+UNFUSED = {"ep2_uneven", "ep3_empty_first_source_empty_expert", "ep2_f32"}
+ALL = [c + (True,) for c in CASES] + [c + (False,) for c in CASES if c[0] in UNFUSED]
+
+
+@pytest.mark.parametrize("name,ep,Ts,d,e_local,k,F,dtype,routing,n_empty,fused", ALL,
+                         ids=[c[0] + ("" if c[-1] else "_unfused") for c in ALL])
+def test_ep_loopback_matches_oracle(name, ep, Ts, d, e_local, k, F, dtype, routing, n_empty, fused):
+    print(f"[ep] {name} fused={fused}: ep={ep} T={Ts} d={d} E_local={e_local} k={k} F={F} {dtype}", flush=True)
     E = ep * e_local
     inp = make_ep_inputs(ep, Ts, d, e_local, k, F, dtype, seed=zlib.crc32(name.encode()) % 10_000, routing=routing,
                          n_empty=n_empty)
     if name == "ep2_idle_destination":  # every token routes to rank 0's experts
         for mb in inp["micro"]:
             mb["logits"][:, e_local:] = np.float32(-1e4)
-    lay, outs, fwd, grads, dw_gu, dw_dn = _run(ep, Ts, d, e_local, k, F, dtype, inp)
+    lay, outs, fwd, grads, dw_gu, dw_dn = _run(ep, Ts, d, e_local, k, F, dtype, inp, fused)
     W = inp["weights"]
     wgu64, wdn64 = to_f64(W["w_gu"], dtype), to_f64(W["w_down"], dtype)
     xs = [to_f64(mb["x"], dtype) for mb in inp["micro"]]

@@ -86,7 +86,7 @@ _SIGNATURES = {
                                       ctypes.c_int32, _P]),
     "moe_ep_exchange_counts_loopback": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "moe_ep_exchange_loopback": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
-                                                ctypes.c_int32, _P]),
+                                                _P, ctypes.c_int32, _P]),
     # include/moe_peak.h
     "moe_peak_mfma": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _P]),
     "moe_peak_mfma_size": (ctypes.c_int64, []),
@@ -285,11 +285,12 @@ def moe_ep_exchange_counts_loopback(ep, e_local, send_counts, recv_counts, strea
 
 
 def moe_ep_exchange_loopback(ep, d, dtype, send_bufs, send_caps, send_offsets, recv_bufs, recv_caps, recv_offsets,
-                             reverse=False, stream=None):
+                             regroup_rows=None, reverse=False, stream=None):
     a = [_ptr_array(send_bufs), _i64_array(send_caps), _ptr_array(send_offsets), _ptr_array(recv_bufs),
          _i64_array(recv_caps), _ptr_array(recv_offsets)]
-    _check(load().moe_ep_exchange_loopback(int(ep), int(d), int(dtype), *[x[0] for x in a], 1 if reverse else 0,
-                                           _stream(stream)), "moe_ep_exchange_loopback")
+    rg = _ptr_array(regroup_rows) if regroup_rows is not None else (None, None)
+    _check(load().moe_ep_exchange_loopback(int(ep), int(d), int(dtype), *[x[0] for x in a], rg[0],
+                                           1 if reverse else 0, _stream(stream)), "moe_ep_exchange_loopback")
 
 
 def moe_peak_mfma_size() -> int:

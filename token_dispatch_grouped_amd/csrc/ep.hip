@@ -110,23 +110,24 @@ __global__ __launch_bounds__(256) void ep_regroup_map_kernel(const int32_t *__re
 
 // Row regroup of the received rows i < recv_offsets[EP]:
 //   forward: dst[regroup_row[i]] = src[i];   reverse: dst[i] = src[regroup_row[i]].
-// One 16-byte chunk per thread, consecutive lanes on consecutive chunks.
+// A workgroup takes whole rows (its row index math is uniform), its threads
+// consecutive 16-byte chunks; the workgroups stride over the rows up to the
+// device total, so a launch sized for the capacity costs nothing past it.
 template <typename T>
 __global__ __launch_bounds__(256) void ep_regroup_kernel(const T *__restrict__ src, T *__restrict__ dst,
                                                          const int32_t *__restrict__ map,
                                                          const int32_t *__restrict__ total, int64_t rows_cap, int nc,
                                                          int reverse) {
   constexpr int V = Elem<T>::kVec;
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t i = g / nc;
-  const int c = (int)(g - i * nc);
-  const int64_t n = *total;
-  if (i >= n || i >= rows_cap) return;
-  const int64_t j = map[i];
-  if ((uint64_t)j >= (uint64_t)rows_cap) return;
+  const int64_t n = min((int64_t)*total, rows_cap);
   const int64_t ld = (int64_t)nc * V;
-  const int64_t from = reverse ? j : i, to = reverse ? i : j;
-  st16(dst + to * ld + (int64_t)c * V, ld16(src + from * ld + (int64_t)c * V));
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
+    const int64_t j = map[i];
+    if ((uint64_t)j >= (uint64_t)rows_cap) continue;
+    const T *from = src + (reverse ? j : i) * ld;
+    T *to = dst + (reverse ? i : j) * ld;
+    for (int c = threadIdx.x; c < nc; c += 256) st16(to + (int64_t)c * V, ld16(from + (int64_t)c * V));
+  }
 }
 
 // Counts exchange stand-in: recv_counts[r][s*E_local + e] = send_counts[s][r*E_local + e].
@@ -142,27 +143,56 @@ __global__ __launch_bounds__(256) void ep_exchange_counts_kernel(EpPtrs send_cou
 }
 
 // Rows exchange stand-in for source s: its row i < send_offsets[EP] belongs
-// to the destination r whose segment holds it and goes to row
-// recv_offsets_r[s] + (i - send_offsets[r]) of r's buffer (reverse: back).
+// to the destination r whose segment holds it; it is received as row
+// recv_offsets_r[s] + (i - send_offsets[r]) of r, and lands at that row of
+// r's buffer, or, when r's regroup map is given, straight at its grouped row
+// regroup_row_r[received row] (one copy instead of an exchange plus a
+// regroup; a multi-GPU peer write can do the same). reverse copies the same
+// rows back. Grid-stride over the source's rows: the host sizes the launch
+// from the source's row count; a workgroup takes one row (uniform index
+// math), its threads consecutive 16-byte chunks.
 template <typename T>
 __global__ __launch_bounds__(256) void ep_exchange_rows_kernel(T *__restrict__ src, const int32_t *__restrict__ send_off,
                                                                int64_t src_cap, EpPtrs dst, EpPtrs recv_off,
-                                                               EpCaps dst_cap, int s, int ep, int nc, int reverse) {
+                                                               EpPtrs regroup, EpCaps dst_cap, int s, int ep, int nc,
+                                                               int reverse) {
   constexpr int V = Elem<T>::kVec;
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t i = g / nc;
-  const int c = (int)(g - i * nc);
+  const int64_t i = blockIdx.x;
   if (i >= src_cap || i >= send_off[ep]) return;
   int r = 0;
   while (r + 1 < ep && i >= send_off[r + 1]) ++r;
-  const int64_t row = static_cast<const int32_t *>(recv_off.p[r])[s] + (i - send_off[r]);
+  int64_t row = static_cast<const int32_t *>(recv_off.p[r])[s] + (i - send_off[r]);
   if ((uint64_t)row >= (uint64_t)dst_cap.n[r]) return;
+  if (regroup.p[r]) {
+    row = static_cast<const int32_t *>(regroup.p[r])[row];
+    if ((uint64_t)row >= (uint64_t)dst_cap.n[r]) return;
+  }
   const int64_t ld = (int64_t)nc * V;
-  T *d = static_cast<T *>(dst.p[r]);
-  if (reverse)
-    st16(src + i * ld + (int64_t)c * V, ld16(d + row * ld + (int64_t)c * V));
-  else
-    st16(d + row * ld + (int64_t)c * V, ld16(src + i * ld + (int64_t)c * V));
+  T *d = static_cast<T *>(dst.p[r]) + row * ld;
+  T *o = src + i * ld;
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    if (reverse)
+      st16(o + (int64_t)c * V, ld16(d + (int64_t)c * V));
+    else
+      st16(d + (int64_t)c * V, ld16(o + (int64_t)c * V));
+  }
+}
+
+// Workgroups of a row-strided copy over up to `rows` rows: at most 16 per
+// CU, fewer for small capacities.
+static unsigned stride_grid(int64_t rows) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  const int64_t want = rows;
+  const int64_t cap = (int64_t)cus * 16;
+  return (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,7 +226,7 @@ hipError_t launch_ep_regroup(const void *src, void *dst, const int32_t *regroup_
                              int64_t rows_cap, int d, bool bf16, bool reverse, hipStream_t s) {
   LaunchScope scope(reverse ? "ep_ungroup" : "ep_regroup", s);
   const int nc = d / (bf16 ? 8 : 4);
-  const unsigned grid = (unsigned)((rows_cap * nc + 255) / 256);
+  const unsigned grid = stride_grid(rows_cap);
   if (bf16)
     ep_regroup_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t *)src, (bf16_t *)dst, regroup_row, total, rows_cap,
                                                    nc, reverse ? 1 : 0);
@@ -214,18 +244,18 @@ hipError_t launch_ep_exchange_counts(const EpPtrs &send_counts, const EpPtrs &re
 }
 
 hipError_t launch_ep_exchange_rows(void *src, const int32_t *send_off, int64_t src_cap, const EpPtrs &dst,
-                                   const EpPtrs &recv_off, const EpCaps &dst_cap, int source, int ep, int d,
-                                   bool bf16, bool reverse, hipStream_t s) {
+                                   const EpPtrs &recv_off, const EpPtrs &regroup, const EpCaps &dst_cap, int source,
+                                   int ep, int d, bool bf16, bool reverse, hipStream_t s) {
   if (src_cap == 0) return hipSuccess;
   LaunchScope scope(reverse ? "ep_return_rows" : "ep_exchange_rows", s);
   const int nc = d / (bf16 ? 8 : 4);
-  const unsigned grid = (unsigned)((src_cap * nc + 255) / 256);
+  const unsigned grid = (unsigned)src_cap;  // one workgroup per row the source can hold (< 2^31)
   if (bf16)
-    ep_exchange_rows_kernel<bf16_t><<<grid, 256, 0, s>>>((bf16_t *)src, send_off, src_cap, dst, recv_off, dst_cap,
-                                                         source, ep, nc, reverse ? 1 : 0);
+    ep_exchange_rows_kernel<bf16_t><<<grid, 256, 0, s>>>((bf16_t *)src, send_off, src_cap, dst, recv_off, regroup,
+                                                         dst_cap, source, ep, nc, reverse ? 1 : 0);
   else
-    ep_exchange_rows_kernel<float><<<grid, 256, 0, s>>>((float *)src, send_off, src_cap, dst, recv_off, dst_cap, source,
-                                                        ep, nc, reverse ? 1 : 0);
+    ep_exchange_rows_kernel<float><<<grid, 256, 0, s>>>((float *)src, send_off, src_cap, dst, recv_off, regroup,
+                                                        dst_cap, source, ep, nc, reverse ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -127,8 +127,8 @@ hipError_t launch_ep_regroup(const void *src, void *dst, const int32_t *regroup_
 hipError_t launch_ep_exchange_counts(const EpPtrs &send_counts, const EpPtrs &recv_counts, int ep, int e_local,
                                      hipStream_t s);
 hipError_t launch_ep_exchange_rows(void *src, const int32_t *send_off, int64_t src_cap, const EpPtrs &dst,
-                                   const EpPtrs &recv_off, const EpCaps &dst_cap, int source, int ep, int d,
-                                   bool bf16, bool reverse, hipStream_t s);
+                                   const EpPtrs &recv_off, const EpPtrs &regroup, const EpCaps &dst_cap, int source,
+                                   int ep, int d, bool bf16, bool reverse, hipStream_t s);
 
 // Attainable-peak probes (peak.hip): a bf16 MFMA loop on `cus` compute
 // units and a plain device copy.

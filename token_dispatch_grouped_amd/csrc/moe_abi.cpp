@@ -580,7 +580,8 @@ moe_status moe_ep_exchange_counts_loopback(int32_t ep, int32_t e_local, const in
 moe_status moe_ep_exchange_loopback(int32_t ep, int32_t d, int32_t dtype, void *const *send_bufs,
                                     const int64_t *send_caps, const int32_t *const *send_offsets,
                                     void *const *recv_bufs, const int64_t *recv_caps,
-                                    const int32_t *const *recv_offsets, int32_t reverse, moe_stream_t stream) {
+                                    const int32_t *const *recv_offsets, const int32_t *const *regroup_rows,
+                                    int32_t reverse, moe_stream_t stream) {
   moe::AbiRange range("moe_ep_exchange_loopback");
   std::string why;
   moe_status st = validate_ep(ep, 1, d, dtype, 0, &why);
@@ -588,7 +589,7 @@ moe_status moe_ep_exchange_loopback(int32_t ep, int32_t d, int32_t dtype, void *
   if (d == 0) return report(MOE_ERR_INVALID_ARGUMENT, "moe_ep_exchange_loopback: d must be positive");
   if (!send_bufs || !send_caps || !send_offsets || !recv_bufs || !recv_caps || !recv_offsets)
     return report(MOE_ERR_INVALID_ARGUMENT, "pointer arrays are NULL");
-  EpPtrs dst{}, roff{};
+  EpPtrs dst{}, roff{}, rgp{};
   EpCaps cap{};
   for (int r = 0; r < ep; ++r) {
     st = validate_ep(ep, 1, d, dtype, send_caps[r], &why);
@@ -603,11 +604,17 @@ moe_status moe_ep_exchange_loopback(int32_t ep, int32_t d, int32_t dtype, void *
     dst.p[r] = recv_bufs[r];
     roff.p[r] = const_cast<int32_t *>(recv_offsets[r]);
     cap.n[r] = recv_caps[r];
+    if (regroup_rows) {
+      const PtrArg rg[] = {{"regroup_rows[r]", regroup_rows[r], recv_caps[r] > 0, false}};
+      st = validate_ptrs(rg, 1, &why);
+      if (st != MOE_OK) return report(st, why);
+      rgp.p[r] = const_cast<int32_t *>(regroup_rows[r]);
+    }
   }
   hipStream_t hs = as_stream(stream);
   for (int s = 0; s < ep; ++s) {
-    st = hip_status(launch_ep_exchange_rows(send_bufs[s], send_offsets[s], send_caps[s], dst, roff, cap, s, ep, d,
-                                            dtype == MOE_DTYPE_BF16, reverse != 0, hs),
+    st = hip_status(launch_ep_exchange_rows(send_bufs[s], send_offsets[s], send_caps[s], dst, roff, rgp, cap, s, ep,
+                                            d, dtype == MOE_DTYPE_BF16, reverse != 0, hs),
                     "ep_exchange_rows");
     if (st != MOE_OK) return st;
   }

@@ -7,19 +7,22 @@ the stream; every step runs in the library's HIP kernels, in this order:
   forward, per source rank s : moe_route (all experts) -> moe_permute -> moe_ep_send_plan
   counts exchange             : moe_ep_exchange_counts_loopback
   per destination rank r      : moe_ep_recv_plan
-  rows exchange               : moe_ep_exchange_loopback
-  per destination rank r      : moe_ep_regroup -> moe_grouped_gemm_fwd -> moe_ep_regroup (reverse)
-  rows back                   : moe_ep_exchange_loopback (reverse)
+  rows exchange               : moe_ep_exchange_loopback (rows land at their grouped rows)
+  per destination rank r      : moe_grouped_gemm_fwd
+  rows back                   : moe_ep_exchange_loopback (reverse, from the grouped rows)
   per source rank s           : moe_unpermute_combine
 
   backward, per source s      : moe_unpermute_combine_bwd -> moe_route_bwd
-  rows exchange (dY)          : moe_ep_exchange_loopback
-  per destination r           : moe_ep_regroup -> moe_grouped_gemm_bwd -> moe_ep_regroup (reverse)
+  rows exchange (dY)          : moe_ep_exchange_loopback (to the grouped rows)
+  per destination r           : moe_grouped_gemm_bwd
   rows back (dX_perm)         : moe_ep_exchange_loopback (reverse)
   per source s                : moe_permute_bwd
 
 The two exchange calls are the one-GPU stand-ins for the all-to-all of the
-counts tables and the all-to-allv of the rows between real ranks. Every rank
+counts tables and the all-to-allv of the rows between real ranks. With
+fused=False the rows land in receive order and moe_ep_regroup moves them to
+the grouped order and back in separate passes (the form for an exchange that
+cannot scatter, e.g. a collective all-to-allv). Every rank
 takes part in every step in the same order whatever its token count, so an
 empty rank never changes the sequence. Buffers are sized once for T_max
 tokens per source; a destination can receive up to EP * T_max * k rows.
@@ -36,8 +39,9 @@ from .layer import torch_dtype
 
 class EpLoopback:
     def __init__(self, ep: int, T_max: int, d: int, e_local: int, k: int, F: int, dtype: int = L.MOE_DTYPE_BF16,
-                 renorm: bool = False, device: str = "cuda"):
+                 renorm: bool = False, fused: bool = True, device: str = "cuda"):
         self.ep, self.T_max, self.d, self.e_local, self.k, self.F = ep, T_max, d, e_local, k, F
+        self.fused = fused
         self.E = ep * e_local
         self.dtype = dtype
         self.flags = L.MOE_FLAG_RENORM if renorm else 0
@@ -80,7 +84,8 @@ class EpLoopback:
                 local_offsets=torch.zeros(e_local + 1, dtype=i32, device=dev),
                 recv_offsets=torch.zeros(ep + 1, dtype=i32, device=dev),
                 regroup_row=torch.empty(cap, dtype=i32, device=dev),
-                recv=torch.empty(cap, d, dtype=td, device=dev),      # received rows (x, then y, dy, dx)
+                # received rows in receive order (x, then y, dy, dx); only without fusion
+                recv=None if fused else torch.empty(cap, d, dtype=td, device=dev),
                 gx=torch.empty(cap, d, dtype=td, device=dev),        # grouped x_perm
                 h=torch.empty(cap, 2 * F, dtype=td, device=dev),
                 a=torch.empty(cap, F, dtype=td, device=dev),
@@ -97,11 +102,30 @@ class EpLoopback:
         """Grouped FFN of one destination: up to rows_cap rows over its E_local experts."""
         return L.make_shape(self.rows_cap, self.d, self.e_local, 1, self.F, self.dtype, 0)
 
-    def _exchange(self, send_key: str, recv_key: str, reverse: bool, stream=None):
-        L.moe_ep_exchange_loopback(
-            self.ep, self.d, self.dtype, [s[send_key] for s in self.src], [t * self.k for t in self.T],
-            [s["send_offsets"] for s in self.src], [r[recv_key] for r in self.dst], [self.rows_cap] * self.ep,
-            [r["recv_offsets"] for r in self.dst], reverse=reverse, stream=stream)
+    def _exchange(self, send_key: str, grouped_key: str, reverse: bool, stream=None):
+        """Rows between the sources' send_key buffers and the destinations'
+        grouped_key buffers; without fusion through the receive buffers and
+        moe_ep_regroup."""
+        ep = self.ep
+        srcs = [s[send_key] for s in self.src]
+        caps = [t * self.k for t in self.T]
+        soffs = [s["send_offsets"] for s in self.src]
+        roffs = [r["recv_offsets"] for r in self.dst]
+        if self.fused:
+            L.moe_ep_exchange_loopback(ep, self.d, self.dtype, srcs, caps, soffs, [r[grouped_key] for r in self.dst],
+                                       [self.rows_cap] * ep, roffs, regroup_rows=[r["regroup_row"] for r in self.dst],
+                                       reverse=reverse, stream=stream)
+            return
+        if reverse:
+            for r in self.dst:
+                L.moe_ep_regroup(self.d, self.dtype, self.rows_cap, ep, r["recv_offsets"], r["regroup_row"],
+                                 r[grouped_key], r["recv"], reverse=True, stream=stream)
+        L.moe_ep_exchange_loopback(ep, self.d, self.dtype, srcs, caps, soffs, [r["recv"] for r in self.dst],
+                                   [self.rows_cap] * ep, roffs, reverse=reverse, stream=stream)
+        if not reverse:
+            for r in self.dst:
+                L.moe_ep_regroup(self.d, self.dtype, self.rows_cap, ep, r["recv_offsets"], r["regroup_row"], r["recv"],
+                                 r[grouped_key], reverse=False, stream=stream)
 
     def forward(self, Ts, xs, logits, w_gu, w_down, stream=None):
         """xs[s] [T_s, d], logits[s] [T_s, E] fp32 of every source; w_gu / w_down
@@ -123,17 +147,13 @@ class EpLoopback:
         for r in self.dst:
             L.moe_ep_recv_plan(ep, el, self.rows_cap, r["recv_counts"], r["local_counts"], r["local_offsets"],
                                r["recv_offsets"], r["regroup_row"], stream)
-        self._exchange("x_perm", "recv", False, stream)
+        self._exchange("x_perm", "gx", False, stream)
         dsh = self.dst_shape()
         for i, r in enumerate(self.dst):
             sl = slice(i * el, (i + 1) * el)
-            L.moe_ep_regroup(self.d, self.dtype, self.rows_cap, ep, r["recv_offsets"], r["regroup_row"], r["recv"],
-                             r["gx"], reverse=False, stream=stream)
             L.moe_grouped_gemm_fwd(dsh, r["gx"], w_gu[sl], w_down[sl], r["local_offsets"], r["h"], r["a"], r["gy"],
                                    r["fwd_ws"], r["fwd_ws"].numel(), stream)
-            L.moe_ep_regroup(self.d, self.dtype, self.rows_cap, ep, r["recv_offsets"], r["regroup_row"], r["gy"],
-                             r["recv"], reverse=True, stream=stream)
-        self._exchange("y_perm", "recv", True, stream)
+        self._exchange("y_perm", "gy", True, stream)
         outs = []
         for s, T in enumerate(self.T):
             b = self.src[s]
@@ -153,17 +173,13 @@ class EpLoopback:
                                         b["dtopk_w"], stream)
             L.moe_route_bwd(sh, b["dtopk_w"], b["logits"], b["topk_idx"], b["topk_w"], None, None, b["dlogits"], None,
                             None, b["route_ws"], b["route_ws"].numel(), stream)
-        self._exchange("dy", "recv", False, stream)
+        self._exchange("dy", "gy", False, stream)
         dsh = self.dst_shape()
         for i, r in enumerate(self.dst):
             sl = slice(i * el, (i + 1) * el)
-            L.moe_ep_regroup(self.d, self.dtype, self.rows_cap, ep, r["recv_offsets"], r["regroup_row"], r["recv"],
-                             r["gy"], reverse=False, stream=stream)
             L.moe_grouped_gemm_bwd(dsh, r["gy"], r["gx"], r["h"], r["a"], w_gu[sl], w_down[sl], r["local_offsets"],
                                    r["gdx"], dw_gu[sl], dw_down[sl], r["bwd_ws"], r["bwd_ws"].numel(), stream)
-            L.moe_ep_regroup(self.d, self.dtype, self.rows_cap, ep, r["recv_offsets"], r["regroup_row"], r["gdx"],
-                             r["recv"], reverse=True, stream=stream)
-        self._exchange("dx_perm", "recv", True, stream)
+        self._exchange("dx_perm", "gdx", True, stream)
         res = []
         for s, T in enumerate(self.T):
             b = self.src[s]
