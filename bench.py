@@ -566,13 +566,24 @@ def main():
     import token_dispatch_grouped_amd as moe
     from workloads import BF16, WORKLOADS
 
-    w = WORKLOADS[args.workload]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.load()
 
     attain = attainable_peaks(dev) if args.attainable else None
+    if args.workload == EP_LOOPBACK["name"]:
+        # the expert-parallel loopback alone: layer TFLOP/s over all simulated ranks
+        r = measure_ep(EP_LOOPBACK, args.steps, args.warmup, attain)
+        line = {"metric": METRIC + " (EP ranks simulated on one GPU)", "value": r.pop("value"), "unit": "TFLOP/s",
+                "n_gpus": 1, "steps": r.pop("steps"), "warmup": args.warmup, "ms_per_step": r.pop("ms_per_step"),
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic", "config": {"workload": EP_LOOPBACK["name"], "seed": EP_LOOPBACK["seed"]},
+                "attainable": attain, "cpu_baseline": None}
+        line.update(r)
+        print(json.dumps(line), flush=True)
+        return
+    w = WORKLOADS[args.workload]
     res, inp = measure(w, args, args.steps, args.warmup, attain, keep_inputs=args.cpu_seconds > 0)
 
     nograd = args.mode == "nograd"
