@@ -122,6 +122,7 @@ template <int BM, int BN, int WM, int WN, int EPI, int NT, int HALF_OFF, typenam
 MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32], u32x4_t *lds, int e, int m0,
                          int n_tile, int m_valid, int64_t crow0, int wm, int wn, NextIssue issue_next) {
   constexpr int WAVES_M = BM / WM;
+  constexpr int WAVES_N = BN / WN;
   constexpr int FM = WM / 32, FN = WN / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -297,160 +298,193 @@ MOE_DEVICE void epilogue(const GemmParams &p, f32x16_t (&acc)[WM / 32][WN / 32],
       flush(std::integral_constant<int, BN / 2>{}, astg + h * WM * (BN / 2), h * WM, p.C2, p.F,
             [&](int c) { return g0 + c < p.N ? g0 + c : -1; });
   } else {  // EPI_SWIGLU_BWD: dA -> dH = (dH_gate | dH_up) using the saved h
-    // The tile is finished in bands through two LDS buffers, each holding a
-    // band's h_gate and h_up tiles ([BR][BN] apiece, chunks swizzled as in
-    // the staging layout). Band b is accumulator row block i = b of every
-    // wavefront row: staged row r is tile row (r / 32) * WM + 32 b + r % 32,
-    // so all wavefronts share the arithmetic of every band. The first half
-    // of the wavefronts only loads (h by LDS DMA, so their vmcnt counts loads
-    // alone and waits in issue order), the second half only stores dH: the h
-    // of band b+1 is in flight while band b is rewritten in place as dH and
-    // then stored.
-    // DMA layout: wave instruction q fills 1 KB = RPI staged rows; lane l
-    // takes physical chunk l % CPR of its row, i.e. logical chunk
-    // phys ^ (row & 15). Rows past m_valid and columns past N are clamped;
-    // their results are never stored. Every valid h element a workgroup
-    // reads lies in its own output tile and is read before the band holding
-    // it is stored, so dH may overwrite h in place (p.C == p.H); a clamped
-    // row may read an already rewritten row, for a result that is dropped.
-    constexpr int BR = WAVES_M * 32;            // rows per band
+    // The tile is finished in bands through two LDS buffers. Band b is
+    // accumulator row block i = b of every wavefront: tile rows
+    // wm * WM + 32 b + (0..31) of both wavefront rows, so every wavefront
+    // rewrites its own 32 x WN sub-block of each band. A buffer holds a band's
+    // h_gate and h_up, each as eight wavefront sub-blocks [32][WN] with the
+    // 16-byte chunks of a sub-block row swizzled by (row & 7).
+    // The first wavefront row (the loaders) only loads: h by LDS DMA, each
+    // loader fetching its own sub-block and the one below it, so its vmcnt
+    // counts loads alone and its own arithmetic needs no other wavefront. The
+    // second row (the storers) only stores. Between workgroup barriers:
+    //   step 0        loaders: DMA bands 0 and 1, wait for band 0
+    //   step 1        everyone: arithmetic of band 0
+    //   step 2b       storers: store band b-1; loaders: wait for band b, its arithmetic
+    //   step 2b+1     storers: arithmetic of band b; loaders: DMA band b+1 into
+    //                 the buffer that band b-1 has just left
+    // so that one row's arithmetic runs beside the other row's memory traffic.
+    // Once band lb0 (the last one in buffer 0, ring slot 0) is read out, the
+    // next tile's first stage is issued there. Rows past m_valid and columns
+    // past N are clamped on load and never stored. Every valid h element a
+    // workgroup reads lies in its own output tile and is read before the band
+    // holding it is stored, so dH may overwrite h in place (p.C == p.H); a
+    // clamped row may read an already rewritten row, for a result that is
+    // dropped.
     constexpr int NBAND = FM;
-    constexpr int HALF = BR * BN;               // elements of one staged half
-    constexpr int BUF = 2 * HALF * 2;           // bytes of one buffer (gate + up)
+    constexpr int SUB = 32 * WN;                  // elements of one wavefront's sub-block
+    constexpr int HALF = WAVES_M * WAVES_N * SUB;  // elements of one staged half (= 32 WAVES_M x BN)
+    constexpr int BUF = 2 * HALF * 2;             // bytes of one buffer (gate + up)
+    constexpr int SCPR = WN / 8;                  // 16-byte chunks per sub-block row
+    constexpr int RPQ = 1024 / (WN * 2);          // sub-block rows per DMA instruction
+    constexpr int QPS = 32 / RPQ;                 // DMA instructions per sub-block and half
+    constexpr int PER_BAND = WAVES_M * QPS * 2;   // DMA instructions per loader and band
+    constexpr int BR = WAVES_M * 32;              // rows per band
     constexpr int CPR = BN / 8;
-    constexpr int RPI = 1024 / (BN * 2);
-    constexpr int NLW = NT / 128;               // loading wavefronts
-    constexpr int NI = BR / (RPI * NLW);        // DMA instructions per loader per half
     constexpr int SCH = 2 * BR * CPR / (NT / 2);  // 16-byte chunks per storing thread
-    constexpr int SB = 8;                       // chunks read from LDS before storing
+    constexpr int SB = 8;                         // chunks read from LDS before storing
+    static_assert(SCPR == 8 && RPQ * QPS == 32, "sub-block rows are one 128-byte line");
+    static_assert(WAVES_N * 64 == NT / 2 && WAVES_M == 2, "one wavefront row loads, the other stores");
     static_assert(2 * BUF <= 160 * 1024, "two band buffers must fit in LDS");
     static_assert(BUF == HALF_OFF, "band buffer 0 is ring slot 0");
-    static_assert(NBAND * BR == BM && NI * RPI * NLW == BR && CPR >= 16, "band shape");
+    static_assert(HALF == BR * BN, "band shape");
     static_assert(SCH * (NT / 2) == 2 * BR * CPR && SCH % SB == 0 && (NT / 2) % CPR == 0, "store split");
     const int n0 = n_tile * BN;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool loader = wv < NLW;
+    const bool loader = wv < WAVES_N;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    auto tile_row = [](int b, int r) { return (r >> 5) * WM + b * 32 + (r & 31); };
-    // Each band takes an opaque copy of the lane index where it is used, so
-    // that no band's addressing is computed early (above the main loop or
-    // for all bands at once) and held in registers beside the accumulators.
+    // element offset of (sub-block row sr, logical chunk c) in sub-block sb
+    auto sub_off = [](int sb, int sr, int c) { return sb * SUB + sr * WN + ((c ^ (sr & 7)) << 3); };
+    // Each use takes an opaque copy of the lane index, so that no band's
+    // addressing is computed early (above the main loop or for all bands at
+    // once) and held in registers beside the accumulators.
     auto issue_band = [&](int b) {
       int lane_e = lane;
       asm volatile("" : "+v"(lane_e));
       const uint32_t base = lds0 + (uint32_t)((b & 1) * BUF);
 #pragma unroll
-      for (int q = 0; q < NI; ++q) {
-        const int r = (q * NLW + wv) * RPI + lane_e / CPR;
-        const int ch = (lane_e % CPR) ^ (r & 15);
-        int gcol = n0 + ch * 8;
-        if (gcol > p.N - 8) gcol = p.N - 8;
-        int rr = tile_row(b, r);
-        if (rr >= m_valid) rr = m_valid - 1;
-        const bf16_t *src = p.H + (crow0 + rr) * p.ldc + gcol;
-        const uint32_t off = (uint32_t)((q * NLW + wv) * 1024);
-        dma16(src, base + off);
-        dma16(src + p.F, base + (uint32_t)(HALF * 2) + off);
+      for (int h2 = 0; h2 < WAVES_M; ++h2) {
+        const int sb = h2 * WAVES_N + wv;
+#pragma unroll
+        for (int q = 0; q < QPS; ++q) {
+          const int sr = q * RPQ + lane_e / SCPR;
+          const int ch = (lane_e % SCPR) ^ (sr & 7);
+          int gcol = n0 + wv * WN + ch * 8;
+          if (gcol > p.N - 8) gcol = p.N - 8;
+          int rr = h2 * WM + b * 32 + sr;
+          if (rr >= m_valid) rr = m_valid - 1;
+          const bf16_t *src = p.H + (crow0 + rr) * p.ldc + gcol;
+          const uint32_t off = (uint32_t)((sb * SUB + q * RPQ * WN) * 2);
+          dma16(src, base + off);
+          dma16(src + p.F, base + (uint32_t)(HALF * 2) + off);
+        }
       }
     };
-    if (loader) {
-      issue_band(0);
-      if (NBAND > 1 && 32 < m_valid) issue_band(1);
-    }
-    // band b holds a valid row iff its first row (tile row 32 b) is valid
-#pragma unroll
-    for (int b = 0; b < NBAND; ++b) {
-      if (b * 32 >= m_valid) break;  // uniform: the later bands hold no valid row
-      const bool next = b + 1 < NBAND && (b + 1) * 32 < m_valid;
-      if (loader) {
-        if (next) wait_vm<2 * NI>();  // band b landed, band b+1 may still fly
-        else wait_vm<0>();
-      }
-      __syncthreads();
-      // last band in buffer 1: buffer 0 (ring slot 0) is read out, so the
-      // next tile's first stage can land there meanwhile
-      if (!next && (b & 1)) issue_next();
+    // the wavefront's own sub-block of band b, h rewritten in place as dH
+    auto arith = [&](int b) {
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
+      const int r = lane_e & 31, hi = lane_e >> 5;
       bf16_t *sg_tile = stg + (b & 1) * (2 * HALF);  // h_gate -> dH_gate
       bf16_t *su_tile = sg_tile + HALF;             // h_up   -> dH_up
-      {
+      const int sb = wm * WAVES_N + wn;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          if (i != b) continue;
-          // the lane's FN*4 groups of four columns; the h of group q+1 is
-          // read from LDS before group q is computed and written back, so
-          // that the read latency overlaps the arithmetic
-          constexpr int NG = FN * 4;
-          auto goff = [&](int q) {  // element offset of group q in either half
-            const int r = wm * 32 + l32;
-            const int col = wn * WN + (q >> 2) * 32 + 8 * (q & 3) + 4 * lhi;
-            return stg_off(r, col, BN);
-          };
-          uint2 hgn = *reinterpret_cast<const uint2 *>(sg_tile + goff(0));
-          uint2 hun = *reinterpret_cast<const uint2 *>(su_tile + goff(0));
+      for (int i = 0; i < FM; ++i) {
+        if (i != b) continue;
+        // the lane's FN*4 groups of four columns (group q = logical chunk q
+        // of the sub-block row, half hi); the h of group q+1 is read from LDS
+        // before group q is computed and written back, so that the read
+        // latency overlaps the arithmetic
+        constexpr int NG = FN * 4;
+        auto goff = [&](int q) { return sub_off(sb, r, q) + 4 * hi; };
+        uint2 hgn = *reinterpret_cast<const uint2 *>(sg_tile + goff(0));
+        uint2 hun = *reinterpret_cast<const uint2 *>(su_tile + goff(0));
 #pragma unroll
-          for (int q = 0; q < NG; ++q) {
-            const uint2 hg2 = hgn, hu2 = hun;
-            if (q + 1 < NG) {
-              hgn = *reinterpret_cast<const uint2 *>(sg_tile + goff(q + 1));
-              hun = *reinterpret_cast<const uint2 *>(su_tile + goff(q + 1));
-            }
-            const int j = q >> 2, g = q & 3;
-            const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
-                                 __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
-            const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
-                                 __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
-            float dg[4], du[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              // t = dA s, dH_up = t hg, dH_gate = t hu (1 + hg (1 - s)) = th + th u
-              // with th = t hu and u = hg - hg s (s = sigmoid(hg))
-              const float sgm = sigmoid_f(hg[v]);
-              const float t = acc[i][j][4 * g + v] * sgm;
-              const float th = t * hu[v];
-              du[v] = t * hg[v];
-              dg[v] = fmaf(th, fmaf(-hg[v], sgm, hg[v]), th);
-            }
-            uint2 og, ou;
-            og.x = pack_bf2(dg[0], dg[1]);
-            og.y = pack_bf2(dg[2], dg[3]);
-            ou.x = pack_bf2(du[0], du[1]);
-            ou.y = pack_bf2(du[2], du[3]);
-            *reinterpret_cast<uint2 *>(sg_tile + goff(q)) = og;
-            *reinterpret_cast<uint2 *>(su_tile + goff(q)) = ou;
+        for (int q = 0; q < NG; ++q) {
+          const uint2 hg2 = hgn, hu2 = hun;
+          if (q + 1 < NG) {
+            hgn = *reinterpret_cast<const uint2 *>(sg_tile + goff(q + 1));
+            hun = *reinterpret_cast<const uint2 *>(su_tile + goff(q + 1));
           }
+          const int j = q >> 2, g = q & 3;
+          const float hg[4] = {__uint_as_float(hg2.x << 16), __uint_as_float(hg2.x & 0xffff0000u),
+                               __uint_as_float(hg2.y << 16), __uint_as_float(hg2.y & 0xffff0000u)};
+          const float hu[4] = {__uint_as_float(hu2.x << 16), __uint_as_float(hu2.x & 0xffff0000u),
+                               __uint_as_float(hu2.y << 16), __uint_as_float(hu2.y & 0xffff0000u)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            // t = dA s, dH_up = t hg, dH_gate = t hu (1 + hg (1 - s)) = th + th u
+            // with th = t hu and u = hg - hg s (s = sigmoid(hg))
+            const float sgm = sigmoid_f(hg[v]);
+            const float t = acc[i][j][4 * g + v] * sgm;
+            const float th = t * hu[v];
+            du[v] = t * hg[v];
+            dg[v] = fmaf(th, fmaf(-hg[v], sgm, hg[v]), th);
+          }
+          uint2 og, ou;
+          og.x = pack_bf2(dg[0], dg[1]);
+          og.y = pack_bf2(dg[2], dg[3]);
+          ou.x = pack_bf2(du[0], du[1]);
+          ou.y = pack_bf2(du[2], du[3]);
+          *reinterpret_cast<uint2 *>(sg_tile + goff(q)) = og;
+          *reinterpret_cast<uint2 *>(su_tile + goff(q)) = ou;
         }
       }
-      __syncthreads();
-      if (!loader) {
-        // thread st stores chunk st % CPR of rows st / CPR + k * (NT/2) / CPR,
-        // gate half first, SB chunks read from LDS before they are stored
-        int st = tid - NT / 2;
-        asm volatile("" : "+v"(st));
-        const int ch = st % CPR;
-        const bool col_ok = n0 + ch * 8 < p.N;
+    };
+    // storers: band b from its buffer to dH, thread st taking chunk st % CPR
+    // of rows st / CPR + k * (NT/2) / CPR, gate half first, SB chunks read
+    // from LDS before they are stored
+    auto store_band = [&](int b) {
+      int st = tid - NT / 2;
+      asm volatile("" : "+v"(st));
+      const bf16_t *buf = stg + (b & 1) * (2 * HALF);
+      const int ch = st % CPR;
+      const bool col_ok = n0 + ch * 8 < p.N;
 #pragma unroll
-        for (int k0 = 0; k0 < SCH; k0 += SB) {
-          u32x4_t v[SB];
+      for (int k0 = 0; k0 < SCH; k0 += SB) {
+        u32x4_t v[SB];
 #pragma unroll
-          for (int k = 0; k < SB; ++k) {
-            const int c = st + (k0 + k) * (NT / 2);
-            const int up = c >= BR * CPR;
-            const int r = (c - up * BR * CPR) / CPR;
-            v[k] = *reinterpret_cast<const u32x4_t *>(sg_tile + up * HALF + r * BN + ((ch ^ (r & 15)) << 3));
-          }
+        for (int k = 0; k < SB; ++k) {
+          const int c = st + (k0 + k) * (NT / 2);
+          const int up = c >= BR * CPR;
+          const int r = (c - up * BR * CPR) / CPR;
+          const int off = up * HALF + sub_off((r >> 5) * WAVES_N + ch / SCPR, r & 31, ch % SCPR);
+          v[k] = *reinterpret_cast<const u32x4_t *>(buf + off);
+        }
 #pragma unroll
-          for (int k = 0; k < SB; ++k) {
-            const int c = st + (k0 + k) * (NT / 2);
-            const int up = c >= BR * CPR;
-            const int r = (c - up * BR * CPR) / CPR;
-            const int tr = tile_row(b, r);
-            if (col_ok && tr < m_valid)
-              st16((bf16_t *)p.C + (crow0 + tr) * p.ldc + (up ? p.F : 0) + n0 + ch * 8, v[k]);
-          }
+        for (int k = 0; k < SB; ++k) {
+          const int c = st + (k0 + k) * (NT / 2);
+          const int up = c >= BR * CPR;
+          const int r = (c - up * BR * CPR) / CPR;
+          const int tr = (r >> 5) * WM + b * 32 + (r & 31);
+          if (col_ok && tr < m_valid)
+            st16((bf16_t *)p.C + (crow0 + tr) * p.ldc + (up ? p.F : 0) + n0 + ch * 8, v[k]);
         }
       }
-      __syncthreads();  // buffer b & 1 has been read out
-      if (loader && b + 2 < NBAND && (b + 2) * 32 < m_valid) issue_band(b + 2);
+    };
+    // bands holding a valid row (band b does iff tile row 32 b is valid)
+    const int nb = min(NBAND, (m_valid + 31) >> 5);
+    const int lb0 = (nb - 1) & ~1;     // last band in buffer 0
+    const int next_step = 2 * lb0 + 3;  // first step after its read-out (never, if past 2 nb)
+    if (loader) {
+      issue_band(0);
+      if (nb > 1) {
+        issue_band(1);
+        wait_vm<PER_BAND>();
+      } else {
+        wait_vm<0>();
+      }
+    }
+    __syncthreads();
+    // unrolled, so that every band index below is a constant and the
+    // accumulators stay in registers
+#pragma unroll
+    for (int s = 1; s <= 2 * NBAND; ++s) {
+      if (s > 2 * nb) break;  // uniform
+      if (s == next_step) issue_next();
+      int band = -1;
+      if (s & 1) {
+        if (!loader || s == 1) band = s >> 1;
+        else if ((s + 1) / 2 < nb) issue_band((s + 1) / 2);
+      } else if (!loader) {
+        store_band(s / 2 - 1);
+      } else if (s / 2 < nb) {
+        wait_vm<0>();  // a loader's only loads in flight are band s/2's
+        band = s / 2;
+      }
+      if (band >= 0) arith(band);
+      if (s < 2 * nb) __syncthreads();
     }
   }
 }
