@@ -70,16 +70,16 @@ ROUTE_TOKENS = 64  # tokens per workgroup of the route pass (its histograms are 
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "26df0d780eb7acba45fa54e98f68a4257e29deceb907aa68d1bc026f2041b7af",
+    "sources_sha256": "82735855132b2045d9600be8d6bd55704443641731de0e30db4a1e5d5a0cf900",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (7.186 + 2.064) * 2 ** 30,
-        "gg_down_fwd": (2.454 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.888 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.709 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (5.048 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.663 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.764 + 2.064) * 2 ** 30,
+        "gg_down_fwd": (2.411 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.449 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (5.728 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (5.071 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.668 + 0.645) * 2 ** 30,
     },
 }
 
