@@ -11,6 +11,8 @@
 // stream. Sums of several rows are formed in fp32 in increasing slot order
 // and rounded once. A row index outside [0, T*k) is skipped rather than
 // followed, so a corrupted dispatch table cannot write out of bounds.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -155,12 +157,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T *__restrict__ 
   }
 }
 
-// B1 for wide rows (at least 256 chunks): one workgroup of NT threads per
+// B1 for rows of 256 to 511 chunks: one workgroup of NT threads per
 // token, thread i taking chunks i, i + NT, ...: a token's rows are then read
 // and written as NT-chunk runs by the whole workgroup, which streams faster
-// than a wavefront walking the row (measured 1% faster at d = 2048, 7% at
-// d = 4096). The k dot products are reduced in each wavefront, then across
-// the wavefronts in a fixed order.
+// than a wavefront walking the row (measured 1% faster at d = 2048). The k
+// dot products are reduced in each wavefront, then across the wavefronts in
+// a fixed order.
 template <typename T, int NT, int KMAX>
 __global__ __launch_bounds__(NT) void combine_bwd_wide_kernel(const T *__restrict__ dout, const T *__restrict__ y,
                                                               const float *__restrict__ tw,
@@ -217,6 +219,81 @@ __global__ __launch_bounds__(NT) void combine_bwd_wide_kernel(const T *__restric
 #pragma unroll
     for (int q = 0; q < NW; ++q) s += part[q][tid];
     dtw[t * k + tid] = s;
+  }
+}
+
+// B1 for rows of 512 or more chunks (d >= 4096 in bf16): one workgroup of 256
+// threads per (token, slot) row, so that each workgroup reads one dout row and one y row,
+// writes one dy row and one dot product, with no dependent work across the
+// token's k rows (2-3% faster at d = 4096 in the layer's step than one
+// workgroup per token walking all k rows; at d = 2048 that form stays, the
+// per-row one measured up to 5% slower there). The hardware hands workgroup b to
+// XCD b % 8; logical row b is token 8 (q / k) + b % 8, slot q % k with
+// q = b / 8, so the k rows of a token run on one XCD and its dout row comes
+// from HBM once and from that XCD's L2 for the other slots. The launch holds
+// a multiple of 8 workgroups, each stepping through the rows gridDim.x apart.
+// A thread takes chunks tid, tid + 256, ... (CPT of them in flight per pass);
+// the dot product is reduced per wavefront, then across the four wavefronts
+// in a fixed order.
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void combine_bwd_row_kernel(const T *__restrict__ dout, const T *__restrict__ y,
+                                                              const float *__restrict__ tw,
+                                                              const int32_t *__restrict__ ros, T *__restrict__ dy,
+                                                              float *__restrict__ dtw, int64_t ntok, int nc, int k,
+                                                              int64_t nlogical) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int NT = 256, NW = NT / 64;
+  __shared__ float part[2][NW];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t ld = (int64_t)nc * V;
+  const int64_t nrows = ntok * k;
+  int it = 0;
+  for (int64_t b = blockIdx.x; b < nlogical; b += gridDim.x, ++it) {
+    const int64_t q = b >> 3;
+    const int64_t grp = q / k;
+    const int64_t t = 8 * grp + (b & 7);
+    const int j = (int)(q - grp * k);
+    if (t >= ntok) continue;  // uniform: past the last token
+    const int64_t row = ros[t * k + j];
+    const float w = tw[t * k + j];
+    float dot = 0.f;
+    if ((uint64_t)row < (uint64_t)nrows) {
+      for (int c0 = 0; c0 < nc; c0 += NT * CPT) {
+        u32x4_t g[CPT], yr[CPT];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+          const int c = c0 + tid + u * NT;
+          if (c < nc) {
+            g[u] = ld16(dout + t * ld + (int64_t)c * V);  // read again by the token's other slots
+            yr[u] = ld16_nt(y + row * ld + (int64_t)c * V);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+          const int c = c0 + tid + u * NT;
+          if (c < nc) {
+            float gv[V], v[V], o[V];
+            Elem<T>::unpack(g[u], gv);
+            Elem<T>::unpack(yr[u], v);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+              dot = fmaf(gv[i], v[i], dot);
+              o[i] = w * gv[i];
+            }
+            st16(dy + row * ld + (int64_t)c * V, Elem<T>::pack(o));
+          }
+        }
+      }
+    }
+    const float ds = wave_sum(dot);
+    if (lane == 0) part[it & 1][wv] = ds;
+    __syncthreads();  // part[it & 1] is rewritten two rows later, after the next barrier
+    if (tid == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < NW; ++q2) s += part[it & 1][q2];
+      dtw[t * k + j] = s;
+    }
   }
 }
 
@@ -327,13 +404,16 @@ static void combine_bwd_c(const T *dout, const T *y, const float *tw, const int3
 template <typename T>
 static void combine_bwd_dispatch(const T *dout, const T *y, const float *tw, const int32_t *ros, T *dy,
                                  float *dtw, int64_t ntok, int nc, int k, hipStream_t s) {
+  if (nc >= 512) {  // one workgroup per (token, slot) row
+    const int64_t nlogical = (ntok + 7) / 8 * 8 * (int64_t)k;
+    const unsigned grid = (unsigned)std::min<int64_t>(nlogical, (int64_t)1 << 20);  // a multiple of 8
+    combine_bwd_row_kernel<T, 2><<<grid, 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k, nlogical);
+    return;
+  }
   if (nc >= 256) {  // one workgroup per token
     with_kmax(k, [&](auto km) {
       constexpr int KM = decltype(km)::value;
-      if (nc >= 512)
-        combine_bwd_wide_kernel<T, 512, KM><<<dim3((unsigned)ntok), 512, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
-      else
-        combine_bwd_wide_kernel<T, 256, KM><<<dim3((unsigned)ntok), 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
+      combine_bwd_wide_kernel<T, 256, KM><<<dim3((unsigned)ntok), 256, 0, s>>>(dout, y, tw, ros, dy, dtw, ntok, nc, k);
     });
     return;
   }
