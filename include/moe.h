@@ -42,7 +42,10 @@
  *    this interface.
  *  - Supported matrix: T >= 0, 1 <= k <= E <= 256, k <= 16, d and F
  *    positive multiples of 64, d <= 65536, F <= 65536, T*k < 2^31,
- *    dtype bf16 or fp32. Anything else returns MOE_ERR_UNSUPPORTED.
+ *    dtype bf16 or fp32, and every launch within 2^32 threads per grid
+ *    dimension: T < 2^24 and T*d < 2^35 (bf16) or 2^34 (fp32), and the
+ *    weight-gradient grid of the grouped GEMM within that bound too.
+ *    Anything else returns MOE_ERR_UNSUPPORTED.
  *  - Calls that overlap on one stream are ordered; calls on different
  *    streams that share buffers race, as with any HIP kernel.
  *
@@ -347,7 +350,7 @@ moe_status moe_aux_loss(const moe_shape *shape, const float *logits, const int32
  * writes that element only: results do not depend on n or on launch layout.
  * Errors: cfg NULL, lr < 0, a beta outside [0, 1), eps <= 0, weight_decay < 0,
  * a non-finite scalar, step < 1 or n < 0 -> MOE_ERR_INVALID_ARGUMENT; unknown
- * flag bits or n >= 2^40 -> MOE_ERR_UNSUPPORTED.
+ * flag bits or n >= 2^35 (a launch of 2^32 threads) -> MOE_ERR_UNSUPPORTED.
  */
 enum { MOE_ADAMW_ZERO_GRAD = 1u };
 
@@ -381,7 +384,9 @@ moe_status moe_adamw_step(const moe_adamw_config *cfg, int64_t n, float *param, 
  * source-major (all of source 0's segment, then source 1's, ...) and runs
  * the grouped FFN on them regrouped by local expert, then source, then their
  * order in the segment. Every count stays on the device; the host passes
- * capacities only. 1 <= EP <= MOE_EP_MAX_RANKS, EP*E_local <= 256.
+ * capacities only. 1 <= EP <= MOE_EP_MAX_RANKS, EP*E_local <= 256, every
+ * row capacity below 2^24 (one 256-thread workgroup per row; larger
+ * capacities return MOE_ERR_UNSUPPORTED).
  */
 enum { MOE_EP_MAX_RANKS = 8 };
 

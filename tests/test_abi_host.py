@@ -77,6 +77,9 @@ def test_ep_argument_rules():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_ep_recv_plan(2, 4, -1, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(moe.MoeError) as ei:   # one workgroup per row: at most 2^24 - 1 rows
+        moe.moe_ep_recv_plan(2, 4, 1 << 24, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
     with pytest.raises(moe.MoeError) as ei:   # overlapping regroup buffers
         moe.moe_ep_regroup(64, L.MOE_DTYPE_BF16, 100, 2, FAKE, FAKE, FAKE, FAKE + 256, stream=0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT and "overlap" in str(ei.value)
@@ -119,11 +122,20 @@ def shape(T=64, d=64, E=4, k=2, F=128, dtype=L.MOE_DTYPE_BF16, flags=0):
     (dict(dtype=7), L.MOE_ERR_UNSUPPORTED),
     (dict(flags=8), L.MOE_ERR_UNSUPPORTED),              # unknown flag bit
     (dict(T=2 ** 28, E=8, k=8), L.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
+    (dict(T=2 ** 24, E=8, k=1), L.MOE_ERR_UNSUPPORTED),  # 256 threads per token: 2^32 threads
+    (dict(T=2 ** 20, d=32768, E=8, k=1), L.MOE_ERR_UNSUPPORTED),  # T*d/8 = 2^32 chunks
+    (dict(T=2 ** 19, d=32768, E=256, k=1, F=32768), L.MOE_ERR_UNSUPPORTED),  # weight-gradient grid
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_workspace_size(shape(**kw))
     assert ei.value.status == status
+
+
+def test_large_shapes_within_the_launch_bounds_are_accepted():
+    # just inside each bound: 2^24 - 1 tokens, T*d/8 just under 2^32
+    moe.moe_workspace_size(shape(T=2 ** 24 - 1, E=8, k=1))
+    moe.moe_workspace_size(shape(T=2 ** 20 - 1, d=32768, E=8, k=1))
 
 
 def test_empty_microbatch_is_a_noop_with_nulls():
@@ -278,7 +290,7 @@ def test_adamw_argument_rules():
         moe.moe_adamw_step(cfg, -1, FAKE, FAKE, FAKE, FAKE, None, stream=0)
     assert ei.value.status == L.MOE_ERR_INVALID_ARGUMENT
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_adamw_step(cfg, 1 << 40, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+        moe.moe_adamw_step(cfg, 1 << 35, FAKE, FAKE, FAKE, FAKE, None, stream=0)
     assert ei.value.status == L.MOE_ERR_UNSUPPORTED
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_adamw_step(cfg, 16, FAKE, None, FAKE, FAKE, None, stream=0)
@@ -365,7 +377,8 @@ int main() {
   moe_adamw_config ab = ac; ab.step = 0; expect(validate_adamw(&ab, 100, &why), MOE_ERR_INVALID_ARGUMENT, "step 0");
   ab = ac; ab.beta2 = 1.f; expect(validate_adamw(&ab, 100, &why), MOE_ERR_INVALID_ARGUMENT, "beta2 1");
   ab = ac; ab.flags = 8; expect(validate_adamw(&ab, 100, &why), MOE_ERR_UNSUPPORTED, "adamw flag");
-  expect(validate_adamw(&ac, (int64_t)1 << 40, &why), MOE_ERR_UNSUPPORTED, "adamw n");
+  expect(validate_adamw(&ac, (int64_t)1 << 35, &why), MOE_ERR_UNSUPPORTED, "adamw n");
+  expect(validate_adamw(&ac, ((int64_t)1 << 35) - 1, &why), MOE_OK, "adamw n below the bound");
   expect(validate_workspace(nullptr, 0, 0, &why), MOE_OK, "no ws needed");
   expect(validate_workspace(nullptr, 0, 16, &why), MOE_ERR_WORKSPACE, "ws null");
   expect(validate_workspace((void*)0x1000, 8, 16, &why), MOE_ERR_WORKSPACE, "ws short");

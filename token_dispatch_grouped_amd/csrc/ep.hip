@@ -249,7 +249,7 @@ hipError_t launch_ep_exchange_rows(void *src, const int32_t *send_off, int64_t s
   if (src_cap == 0) return hipSuccess;
   LaunchScope scope(reverse ? "ep_return_rows" : "ep_exchange_rows", s);
   const int nc = d / (bf16 ? 8 : 4);
-  const unsigned grid = (unsigned)src_cap;  // one workgroup per row the source can hold (< 2^31)
+  const unsigned grid = (unsigned)src_cap;  // one workgroup per row the source can hold (< 2^24)
   if (bf16)
     ep_exchange_rows_kernel<bf16_t><<<grid, 256, 0, s>>>((bf16_t *)src, send_off, src_cap, dst, recv_off, regroup,
                                                          dst_cap, source, ep, nc, reverse ? 1 : 0);

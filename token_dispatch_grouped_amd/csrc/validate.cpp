@@ -39,19 +39,28 @@ moe_status validate_shape(const moe_shape *s, std::string *why) {
   const int64_t lim = ((int64_t)1 << 31) - 1;
   const int64_t wide = s->d > 2 * (int64_t)s->F ? s->d : 2 * (int64_t)s->F;
   int64_t gemm_blocks;
+  int64_t gemm_threads;  // threads of the largest grouped-GEMM launch that is not persistent
   if (s->dtype == MOE_DTYPE_BF16) {
     const int64_t slots = ceil_div(R / kGemmBM + s->E, kGemmGroupM) * kGemmGroupM;
     gemm_blocks = ceil_div(slots * ceil_div(wide, kGemmBN / 2), 8) * 8;
     const int64_t wg = ceil_div((int64_t)s->E * ceil_div(wide, kGemmBM) * ceil_div(wide, kGemmBN), 64) * 64;
     if (wg > gemm_blocks) gemm_blocks = wg;
+    gemm_threads = wg * 512;  // the ragged-M products run one 512-thread workgroup per CU
   } else {
     gemm_blocks = (R / kGemmF32Tile + s->E) * ceil_div(wide, kGemmF32Tile);
     const int64_t wg = (int64_t)s->E * ceil_div(wide, kGemmF32Tile) * ceil_div(wide, kGemmF32Tile);
     if (wg > gemm_blocks) gemm_blocks = wg;
+    gemm_threads = gemm_blocks * 256;
   }
   const int64_t vec = s->dtype == MOE_DTYPE_BF16 ? 8 : 4;
   const int64_t mem_blocks = ceil_div(s->T * (s->d / vec), 256);
   if (gemm_blocks > lim || mem_blocks > lim) return fail(why, MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+  // a grid dimension holds fewer than 2^32 threads: the per-token launches
+  // (256 threads per token at most), the one-thread-per-chunk memory kernels
+  // and the non-persistent grouped GEMM grids
+  const int64_t items = (int64_t)1 << 32;
+  if (s->T * 256 >= items || s->T * (s->d / vec) >= items || gemm_threads >= items)
+    return fail(why, MOE_ERR_UNSUPPORTED, "problem too large for one launch (2^32 threads per grid dimension)");
   return MOE_OK;
 }
 
@@ -117,7 +126,8 @@ moe_status validate_workspace(const void *ws, size_t have, size_t need, std::str
 moe_status validate_adamw(const moe_adamw_config *c, int64_t n, std::string *why) {
   if (!c) return fail(why, MOE_ERR_INVALID_ARGUMENT, "adamw config is NULL");
   if (n < 0) return fail(why, MOE_ERR_INVALID_ARGUMENT, "negative element count");
-  if (n >= ((int64_t)1 << 40)) return fail(why, MOE_ERR_UNSUPPORTED, "element count >= 2^40");
+  // eight elements per thread: 2^35 elements fill a grid of 2^32 threads
+  if (n >= ((int64_t)1 << 35)) return fail(why, MOE_ERR_UNSUPPORTED, "element count >= 2^35");
   if (c->flags & ~(uint32_t)MOE_ADAMW_ZERO_GRAD) return fail(why, MOE_ERR_UNSUPPORTED, "unknown adamw flag bits");
   const float vals[] = {c->lr, c->beta1, c->beta2, c->eps, c->weight_decay, c->grad_scale};
   for (float v : vals)
@@ -142,7 +152,8 @@ moe_status validate_ep(int32_t ep, int32_t e_local, int32_t d, int32_t dtype, in
       return fail(why, MOE_ERR_UNSUPPORTED, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   }
   if (rows_cap < 0) return fail(why, MOE_ERR_INVALID_ARGUMENT, "negative row capacity");
-  if (rows_cap >= ((int64_t)1 << 31)) return fail(why, MOE_ERR_UNSUPPORTED, "row capacity >= 2^31");
+  // one 256-thread workgroup per row: 2^24 rows fill a grid of 2^32 threads
+  if (rows_cap >= ((int64_t)1 << 24)) return fail(why, MOE_ERR_UNSUPPORTED, "row capacity >= 2^24");
   return MOE_OK;
 }
 
