@@ -253,7 +253,9 @@ __global__ __launch_bounds__(256) void combine_bwd_row_kernel(const T *__restric
     const int64_t grp = q / k;
     const int64_t t = 8 * grp + (b & 7);
     const int j = (int)(q - grp * k);
-    if (t >= ntok) continue;  // uniform: past the last token
+    // uniform, and final: the token index only grows along a workgroup's rows
+    // (b % 8 is fixed because gridDim.x is a multiple of 8)
+    if (t >= ntok) break;
     const int64_t row = ros[t * k + j];
     const float w = tw[t * k + j];
     float dot = 0.f;
