@@ -175,6 +175,13 @@ SMALL_CASES = [
     # and d = 8256 in fp32 take a second pass over the row's last chunks
     ("bf16_wide_d16448", small_workload(6, 16448, 4, 2, 64, BF16, "normal", seed=39), False),
     ("f32_wide_d8256", small_workload(5, 8256, 3, 2, 64, F32, "normal", seed=40), False),
+    # the combine backward's three forms at their edges: one workgroup per token with a ragged second pass
+    # (264 and 272 chunks), one workgroup per (token, slot) row with a ragged second chunk loop (520 chunks),
+    # k = 3 and T = 13 so logical rows past the last token end the loop, and the per-row form in fp32
+    ("bf16_d2112_cbwd_token_tail", small_workload(9, 2112, 4, 2, 64, BF16, "normal", seed=41), False),
+    ("f32_d1088_cbwd_token_tail", small_workload(7, 1088, 3, 2, 64, F32, "normal", seed=42), False),
+    ("bf16_d4160_cbwd_row_tail", small_workload(13, 4160, 5, 3, 64, BF16, "normal", seed=43), False),
+    ("f32_d2048_cbwd_row", small_workload(11, 2048, 4, 1, 64, F32, "zipf", seed=44), False),
 ]
 
 
