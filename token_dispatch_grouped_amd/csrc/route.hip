@@ -69,36 +69,125 @@ MOE_DEVICE uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Visit row[0..E) in ascending order, f(e, value). With E % 4 == 0 (rows
-// then 16-byte aligned) the row is read 16 values at a time by four 16-byte
-// loads issued together, so that a thread waits for one round trip per 16
-// values instead of one per value.
-template <typename F>
-MOE_DEVICE void for_row(const float *__restrict__ row, int E, F f) {
-  int e0 = 0;
-  if ((E & 3) == 0) {
-    for (; e0 + 16 <= E; e0 += 16) {
-      float4 v[4];
+// Inverse of order_key: the logit a key stands for (-0.0 comes back as +0.0,
+// every NaN as one NaN).
+MOE_DEVICE float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Lanes G that share one token's logit row: the smallest power of two that
+// leaves each lane at most eight logits, at most eight lanes; and the most
+// logits V one lane then holds (8, or 16 / 32 for rows of more than 64).
+constexpr int route_lanes(int E) { return E <= 8 ? 1 : E <= 16 ? 2 : E <= 32 ? 4 : 8; }
+constexpr int route_lane_values(int E) { return E <= 64 ? 8 : E <= 128 ? 16 : 32; }
+template <int G, int V>
+struct RouteLane {
+  static constexpr int kValues = V;
+  // The row element that value i of lane g holds: with 16-byte rows
+  // (E % 4 == 0) the chunks g, g + G, ... of four values, so that the G lanes
+  // of a row read consecutive 16-byte chunks; else the values g, g + G, ...
+  MOE_DEVICE static int elem(int i, int g, bool vec) { return vec ? 4 * (g + G * (i >> 2)) + (i & 3) : g + G * i; }
+  // All of the lane's loads are issued before any is used: one round trip.
+  template <typename P>
+  MOE_DEVICE static void load(P *__restrict__ row, int E, int g, bool vec, float (&v)[kValues]) {
+    if (vec) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const float4 *>(row + e0 + 4 * i);
+      for (int c = 0; c < kValues / 4; ++c) {
+        const int e = 4 * (g + G * c);
+        const float4 x = e < E ? *reinterpret_cast<const float4 *>(row + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[4 * c] = x.x;
+        v[4 * c + 1] = x.y;
+        v[4 * c + 2] = x.z;
+        v[4 * c + 3] = x.w;
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f(e0 + 4 * i, v[i].x);
-        f(e0 + 4 * i + 1, v[i].y);
-        f(e0 + 4 * i + 2, v[i].z);
-        f(e0 + 4 * i + 3, v[i].w);
+      for (int i = 0; i < kValues; ++i) {
+        const int e = g + G * i;
+        v[i] = e < E ? row[e] : 0.f;
       }
     }
-    for (; e0 < E; e0 += 4) {
-      const float4 v = *reinterpret_cast<const float4 *>(row + e0);
-      f(e0, v.x);
-      f(e0 + 1, v.y);
-      f(e0 + 2, v.z);
-      f(e0 + 3, v.w);
-    }
-    return;
   }
-  for (; e0 < E; ++e0) f(e0, row[e0]);
+};
+
+MOE_DEVICE uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+MOE_DEVICE uint64_t min_u64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// Bitonic sorting network over N (a power of two) keys, descending.
+template <int N>
+MOE_DEVICE void sort_desc(uint64_t (&c)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t x = c[i], y = c[j];
+          const bool desc = (i & size) == 0;  // the last stage sorts all N descending
+          c[i] = desc ? max_u64(x, y) : min_u64(x, y);
+          c[j] = desc ? min_u64(x, y) : max_u64(x, y);
+        }
+      }
+    }
+  }
+}
+
+// Keep the KMAX largest of two descending key lists in `a`, descending. The
+// larger of a[i] and b[KMAX-1-i] over all i are the KMAX largest of both
+// lists and form a bitonic sequence, which log2(KMAX) half-cleaner stages put
+// in descending order. Swapping the two lists gives the same result.
+template <int KMAX>
+MOE_DEVICE void merge_topk(uint64_t (&a)[KMAX], const uint64_t (&b)[KMAX]) {
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) a[i] = max_u64(a[i], b[KMAX - 1 - i]);
+#pragma unroll
+  for (int h = KMAX / 2; h > 0; h >>= 1) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if ((i & h) == 0) {
+        const uint64_t x = a[i], y = a[i + h];
+        a[i] = max_u64(x, y);
+        a[i + h] = min_u64(x, y);
+      }
+    }
+  }
+}
+
+// merge_topk with the list of the lane `s` away (same wavefront).
+template <int KMAX>
+MOE_DEVICE void merge_topk_xor(uint64_t (&a)[KMAX], int s) {
+  uint64_t b[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const uint32_t lo = __shfl_xor((uint32_t)a[i], s);
+    const uint32_t hi = __shfl_xor((uint32_t)(a[i] >> 32), s);
+    b[i] = ((uint64_t)hi << 32) | lo;
+  }
+  merge_topk<KMAX>(a, b);
+}
+
+// The KMAX largest of V keys (V a multiple of 8), descending, padded with 0:
+// each run of eight sorted by a network, the runs' KMAX largest merged.
+template <int KMAX, int V>
+MOE_DEVICE void local_topk(const uint64_t (&c)[V], uint64_t (&list)[KMAX]) {
+#pragma unroll
+  for (int r = 0; r < V / 8; ++r) {
+    uint64_t run[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) run[i] = c[8 * r + i];
+    sort_desc<8>(run);
+    uint64_t top[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) top[i] = i < 8 ? run[i] : 0ull;
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) list[i] = top[i];
+    } else {
+      merge_topk<KMAX>(list, top);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -106,66 +195,77 @@ MOE_DEVICE void for_row(const float *__restrict__ row, int E, F f) {
 // stable rank of each (token, slot) among the workgroup's slots of the same
 // expert, and the workgroup's expert histogram.
 //
-// One thread per token, kRouteTokensPerBlock tokens per workgroup (one
-// wavefront: 512 workgroups at 32k tokens, so every CU gets work). Top-k keeps
-// a descending list of 64-bit composite keys (logit key, then inverted id so
-// that the lower id wins a tie). A token selects an expert at most once, so
-// the rank of slot (t, j) among the workgroup's slots of expert e is the
-// number of earlier tokens of the workgroup that selected e. Each wavefront
-// builds in LDS, per expert, the 64-bit mask of its lanes that selected it
-// (bitwise OR, whose result does not depend on the order of the updates);
-// the rank is the population count of the masks of earlier wavefronts plus
-// that of the own mask below the lane. No atomic decides any order.
+// kRouteTokensPerBlock tokens per workgroup, G = route_lanes(E) lanes per
+// token. A lane reads its share of the logit row in one round of 16-byte
+// loads and sorts the 64-bit composite keys of its share (logit key, then
+// inverted id, so that the lower id wins a tie) in runs of eight with a
+// sorting network, keeping the k largest; the G lanes then merge their k
+// largest pairwise over a butterfly, after which every lane holds the token's
+// top k. The softmax maximum is the first key's logit; the
+// sum of exponentials is added up per lane and then over the butterfly (each
+// pair adds the same two terms, so every lane gets the same sum). Lane g
+// writes slots g, g + G, ...
+//
+// A token selects an expert at most once, so the rank of slot (t, j) among
+// the workgroup's slots of expert e is the number of earlier tokens of the
+// workgroup that selected e: each slot sets its token's bit in expert e's
+// 64-bit mask in LDS (bitwise OR, whose result does not depend on the order
+// of the updates) and the rank is the population count of the mask below the
+// token's bit. No atomic decides any order.
 // ---------------------------------------------------------------------------
-template <int KMAX>
-__global__ __launch_bounds__(kRouteTokensPerBlock) void route_topk_kernel(const float *__restrict__ logits,
-                                                         int32_t *__restrict__ topk_idx,
-                                                         float *__restrict__ topk_w,
-                                                         int32_t *__restrict__ local_rank,
-                                                         int32_t *__restrict__ blk_cnt, int64_t ntok, int E,
-                                                         int k, int renorm) {
-  constexpr int NT = kRouteTokensPerBlock;
-  constexpr int NW = NT / 64;
-  static_assert(NW * 64 == NT, "whole wavefronts per workgroup");
-  __shared__ unsigned long long s_mask[NW][256];
+template <int KMAX, int G, int V>
+__global__ __launch_bounds__(kRouteTokensPerBlock *G) void route_topk_kernel(const float *__restrict__ logits,
+                                                                 int32_t *__restrict__ topk_idx,
+                                                                 float *__restrict__ topk_w,
+                                                                 int32_t *__restrict__ local_rank,
+                                                                 int32_t *__restrict__ blk_cnt, int64_t ntok,
+                                                                 int E, int k, int renorm) {
+  static_assert(kRouteTokensPerBlock == 64, "one bit per token of the workgroup in a 64-bit mask");
+  constexpr int NT = kRouteTokensPerBlock * G;
+  using Lane = RouteLane<G, V>;
+  __shared__ unsigned long long s_mask[256];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int64_t t = (int64_t)blockIdx.x * NT + tid;
-  const bool valid = t < ntok;
+  const int g = tid % G;
+  const int tl = tid / G;  // token within the workgroup
+  const int64_t t = (int64_t)blockIdx.x * kRouteTokensPerBlock + tl;
+  const bool valid = t < ntok;  // the same for the G lanes of a token
+  const bool vec = (E & 3) == 0;
 
-  for (int i = tid; i < NW * 256; i += NT) (&s_mask[0][0])[i] = 0ull;
+  for (int i = tid; i < E; i += NT) s_mask[i] = 0ull;
 
+  float v[V];
+  uint64_t c[V];
+  if (valid) Lane::load(logits + t * E, E, g, vec, v);
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = Lane::elem(i, g, vec);
+    // 0 lies below every real key: values past the row and rows past the end
+    c[i] = (valid && e < E) ? ((uint64_t)order_key(v[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+  }
   uint64_t list[KMAX];
+  local_topk<KMAX, V>(c, list);
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) list[i] = 0ull;
+  for (int s = 1; s < G; s <<= 1) merge_topk_xor<KMAX>(list, s);
+
   int ids[KMAX];
-  float w[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) ids[i] = (int)(0xffffffffu - (uint32_t)(list[i] & 0xffffffffu));
   if (valid) {
-    const float *row = logits + t * E;
-    for_row(row, E, [&](int e, float l) {
-      uint64_t c = ((uint64_t)order_key(l) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
-      if (c > list[KMAX - 1]) {
-        // insert into the descending list: entries above c stay, c takes the
-        // first place it beats, the entries below shift down one place
-        bool g[KMAX];
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) g[i] = c > list[i];
-#pragma unroll
-        for (int i = KMAX - 1; i > 0; --i) list[i] = g[i - 1] ? list[i - 1] : (g[i] ? c : list[i]);
-        list[0] = g[0] ? c : list[0];
-      }
-    });
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) ids[i] = (int)(0xffffffffu - (uint32_t)(list[i] & 0xffffffffu));
     // softmax over the whole row; the first selected logit is the maximum
-    const float m = row[ids[0]];
+    const float m = key_value((uint32_t)(list[0] >> 32));
     float sum = 0.f;
-    for_row(row, E, [&](int, float l) { sum += (l == l) ? expf(l - m) : 0.f; });
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = Lane::elem(i, g, vec);
+      if (e < E && v[i] == v[i]) sum += expf(v[i] - m);
+    }
+#pragma unroll
+    for (int s = 1; s < G; s <<= 1) sum += __shfl_xor(sum, s);
+    float w[KMAX];
     float wsum = 0.f;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
-      float l = row[(unsigned)ids[i] < (unsigned)E ? ids[i] : 0];
+      const float l = key_value((uint32_t)(list[i] >> 32));
       w[i] = (i < k && l == l) ? expf(l - m) / sum : 0.f;
       if (i < k) wsum += w[i];
     }
@@ -175,39 +275,26 @@ __global__ __launch_bounds__(kRouteTokensPerBlock) void route_topk_kernel(const 
     }
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
-      if (i < k) {
+      if (i < k && i % G == g) {
         topk_idx[t * k + i] = ids[i];
         topk_w[t * k + i] = w[i];
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) ids[i] = 0;
   }
   __syncthreads();  // masks cleared
   if (valid) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < k) atomicOr(&s_mask[wave][ids[j]], 1ull << lane);
+    for (int i = 0; i < KMAX; ++i)
+      if (i < k && i % G == g) atomicOr(&s_mask[ids[i]], 1ull << tl);
   }
   __syncthreads();
   if (valid) {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t below = (1ull << tl) - 1ull;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
-        int pre = __popcll(s_mask[wave][ids[j]] & below);
-        for (int w2 = 0; w2 < wave; ++w2) pre += __popcll(s_mask[w2][ids[j]]);
-        local_rank[t * k + j] = pre;
-      }
-    }
+    for (int i = 0; i < KMAX; ++i)
+      if (i < k && i % G == g) local_rank[t * k + i] = __popcll(s_mask[ids[i]] & below);
   }
-  for (int e = tid; e < E; e += NT) {
-    int c = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) c += __popcll(s_mask[w2][e]);
-    blk_cnt[(int64_t)blockIdx.x * E + e] = c;
-  }
+  for (int e = tid; e < E; e += NT) blk_cnt[(int64_t)blockIdx.x * E + e] = __popcll(s_mask[e]);
 }
 
 // Block-wide exclusive scan of one int per thread (256 threads); returns the
@@ -280,77 +367,112 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const int32_t *__restri
 }
 
 // ---------------------------------------------------------------------------
-// B2: dlogits from dtopk_w. One thread per token.
+// B2: dlogits from dtopk_w. route_lanes(E) lanes per token as in the top-k:
+// each lane holds its share of the logit row in registers, the row maximum
+// and the sum of exponentials are reduced over the token's lanes, and each
+// lane writes its share of the dlogits row.
 // ---------------------------------------------------------------------------
-constexpr int kRouteBwdThreads = 64;  // one wavefront per workgroup: 512 workgroups at 32k tokens
+constexpr int kRouteBwdThreads = 256;
 
-template <int KMAX>
+template <int KMAX, int G, int V>
 __global__ __launch_bounds__(kRouteBwdThreads) void route_bwd_kernel(const float *__restrict__ dtopk_w,
                                                         const float *__restrict__ logits,
                                                         const int32_t *__restrict__ topk_idx,
                                                         const float *__restrict__ topk_w,
                                                         float *__restrict__ dlogits, int64_t ntok, int E, int k,
                                                         int renorm, int accumulate) {
-  const int64_t t = (int64_t)blockIdx.x * kRouteBwdThreads + threadIdx.x;
+  using Lane = RouteLane<G, V>;
+  const int g = threadIdx.x % G;
+  const int64_t t = ((int64_t)blockIdx.x * kRouteBwdThreads + threadIdx.x) / G;
+  // a token's G lanes leave together, so the reductions below only ever
+  // exchange values between lanes that stay
   if (t >= ntok) return;
+  const bool vec = (E & 3) == 0;
   const float *row = logits + t * E;
   float *drow = dlogits + t * E;
   int ids[KMAX];
-  float g[KMAX], w[KMAX];
+  float gk[KMAX], wk[KMAX];
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
+    ids[j] = -1;
+    gk[j] = wk[j] = 0.f;
     if (j < k) {
       ids[j] = topk_idx[t * k + j];
-      g[j] = dtopk_w[t * k + j];
-      w[j] = topk_w[t * k + j];
-      s = fmaf(w[j], g[j], s);
+      gk[j] = dtopk_w[t * k + j];
+      wk[j] = topk_w[t * k + j];
+      s = fmaf(wk[j], gk[j], s);
     }
   }
+  float old[V];
+  if (accumulate)
+    Lane::load(drow, E, g, vec, old);
+  else
+#pragma unroll
+    for (int i = 0; i < V; ++i) old[i] = 0.f;
+  float d[V];
   if (renorm) {
-    if (!accumulate) {
-      if ((E & 3) == 0)
-        for (int e = 0; e < E; e += 4) *reinterpret_cast<float4 *>(drow + e) = make_float4(0.f, 0.f, 0.f, 0.f);
-      else
-        for (int e = 0; e < E; ++e) drow[e] = 0.f;
-    }
+    // only the selected logits carry a gradient: w_j (g_j - s)
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < k) drow[ids[j]] = accumulate ? drow[ids[j]] + w[j] * (g[j] - s) : w[j] * (g[j] - s);
-    return;
-  }
-  // accumulate: what dlogits held at the selected ids, before the first pass
-  float base[KMAX];
+    for (int i = 0; i < V; ++i) {
+      const int e = Lane::elem(i, g, vec);
+      bool sel = false;
+      float x = 0.f;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) base[j] = (accumulate && j < k) ? drow[ids[j]] : 0.f;
-  float m = -INFINITY;
-  for_row(row, E, [&](int, float l) {
-    if (l == l) m = fmaxf(m, l);
-  });
-  float sum = 0.f;
-  for_row(row, E, [&](int, float l) { sum += (l == l) ? expf(l - m) : 0.f; });
-  const float inv = 1.f / sum;
-  auto dval = [&](float l, float old) {
-    const float p = (l == l) ? expf(l - m) * inv : 0.f;
-    return accumulate ? old - p * s : -p * s;
-  };
-  if ((E & 3) == 0) {  // 16-byte rows: four values per load and store
-    for (int e = 0; e < E; e += 4) {
-      const float4 l = *reinterpret_cast<const float4 *>(row + e);
-      float4 o = {0.f, 0.f, 0.f, 0.f};
-      if (accumulate) o = *reinterpret_cast<const float4 *>(drow + e);
-      *reinterpret_cast<float4 *>(drow + e) =
-          make_float4(dval(l.x, o.x), dval(l.y, o.y), dval(l.z, o.z), dval(l.w, o.w));
+      for (int j = 0; j < KMAX; ++j) {
+        if (ids[j] == e) {
+          sel = true;
+          x = wk[j] * (gk[j] - s);
+        }
+      }
+      d[i] = sel ? (accumulate ? old[i] + x : x) : old[i];
     }
   } else {
-    for (int e = 0; e < E; ++e) drow[e] = dval(row[e], accumulate ? drow[e] : 0.f);
-  }
+    float l[V];
+    Lane::load(row, E, g, vec, l);
+    float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      float l = row[ids[j]];
-      float p = (l == l) ? expf(l - m) * inv : 0.f;
-      drow[ids[j]] = accumulate ? base[j] + p * (g[j] - s) : p * (g[j] - s);
+    for (int i = 0; i < V; ++i)
+      if (Lane::elem(i, g, vec) < E && l[i] == l[i]) m = fmaxf(m, l[i]);
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (Lane::elem(i, g, vec) < E && l[i] == l[i]) sum += expf(l[i] - m);
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) sum += __shfl_xor(sum, o);
+    const float inv = 1.f / sum;
+    // p_e (g_e - s): g_e = dtopk_w of the slot that selected e, else 0
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = Lane::elem(i, g, vec);
+      const float p = (l[i] == l[i]) ? expf(l[i] - m) * inv : 0.f;
+      bool sel = false;
+      float ge = 0.f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (ids[j] == e) {
+          sel = true;
+          ge = gk[j];
+        }
+      }
+      const float x = sel ? p * (ge - s) : -(p * s);
+      d[i] = accumulate ? old[i] + x : x;
+    }
+  }
+  if (vec) {
+#pragma unroll
+    for (int c = 0; c < V / 4; ++c) {
+      const int e = 4 * (g + G * c);
+      if (e < E)
+        *reinterpret_cast<float4 *>(drow + e) = make_float4(d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = g + G * i;
+      if (e < E) drow[e] = d[i];
     }
   }
 }
@@ -424,12 +546,25 @@ hipError_t launch_router_logits(const void *x, const void *w_router, const float
   return hipGetLastError();
 }
 
+template <int KMAX, int G, int V>
+static void launch_topk_kg(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *rank, int32_t *blk_cnt,
+                           int64_t T, int E, int k, int r, hipStream_t s) {
+  route_topk_kernel<KMAX, G, V><<<dim3((unsigned)route_blocks(T)), kRouteTokensPerBlock * G, 0, s>>>(
+      logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r);
+}
+
 template <int KMAX>
 static void launch_topk_k(const float *logits, int32_t *topk_idx, float *topk_w, int32_t *rank, int32_t *blk_cnt,
                           int64_t T, int E, int k, bool renorm, hipStream_t s) {
-  dim3 grid((unsigned)route_blocks(T));
-  route_topk_kernel<KMAX><<<grid, kRouteTokensPerBlock, 0, s>>>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k,
-                                                                 renorm ? 1 : 0);
+  const int r = renorm ? 1 : 0;
+  switch (route_lanes(E) * route_lane_values(E)) {  // (G, V): (1, 8) (2, 8) (4, 8) (8, 8) (8, 16) (8, 32)
+    case 8: launch_topk_kg<KMAX, 1, 8>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r, s); break;
+    case 16: launch_topk_kg<KMAX, 2, 8>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r, s); break;
+    case 32: launch_topk_kg<KMAX, 4, 8>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r, s); break;
+    case 64: launch_topk_kg<KMAX, 8, 8>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r, s); break;
+    case 128: launch_topk_kg<KMAX, 8, 16>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r, s); break;
+    default: launch_topk_kg<KMAX, 8, 32>(logits, topk_idx, topk_w, rank, blk_cnt, T, E, k, r, s); break;
+  }
 }
 
 // Scratch of the allocation-free routing entry point (moe_route_noalloc):
@@ -494,20 +629,42 @@ hipError_t launch_route(const float *logits, int32_t *topk_idx, float *topk_w, i
   return hipGetLastError();
 }
 
+template <int KMAX, int G, int V>
+static void launch_route_bwd_kg(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
+                                const float *topk_w, float *dlogits, int64_t T, int E, int k, int r, int a,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)((T * G + kRouteBwdThreads - 1) / kRouteBwdThreads));
+  route_bwd_kernel<KMAX, G, V><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k,
+                                                              r, a);
+}
+
+template <int KMAX>
+static void launch_route_bwd_k(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
+                               const float *topk_w, float *dlogits, int64_t T, int E, int k, int r, int a,
+                               hipStream_t s) {
+  switch (route_lanes(E) * route_lane_values(E)) {  // (G, V) as in the top-k
+    case 8: launch_route_bwd_kg<KMAX, 1, 8>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s); break;
+    case 16: launch_route_bwd_kg<KMAX, 2, 8>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s); break;
+    case 32: launch_route_bwd_kg<KMAX, 4, 8>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s); break;
+    case 64: launch_route_bwd_kg<KMAX, 8, 8>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s); break;
+    case 128: launch_route_bwd_kg<KMAX, 8, 16>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s); break;
+    default: launch_route_bwd_kg<KMAX, 8, 32>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s); break;
+  }
+}
+
 hipError_t launch_route_bwd(const float *dtopk_w, const float *logits, const int32_t *topk_idx,
                             const float *topk_w, float *dlogits, int64_t T, int E, int k, bool renorm,
                             bool accumulate, hipStream_t s) {
   LaunchScope scope("route_bwd", s);
-  dim3 grid((unsigned)((T + kRouteBwdThreads - 1) / kRouteBwdThreads));
   const int r = renorm ? 1 : 0, a = accumulate ? 1 : 0;
   if (k <= 2)
-    route_bwd_kernel<2><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    launch_route_bwd_k<2>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s);
   else if (k <= 4)
-    route_bwd_kernel<4><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    launch_route_bwd_k<4>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s);
   else if (k <= 8)
-    route_bwd_kernel<8><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    launch_route_bwd_k<8>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s);
   else
-    route_bwd_kernel<16><<<grid, kRouteBwdThreads, 0, s>>>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a);
+    launch_route_bwd_k<16>(dtopk_w, logits, topk_idx, topk_w, dlogits, T, E, k, r, a, s);
   return hipGetLastError();
 }
 
