@@ -35,7 +35,8 @@ exchanges as device copies; the exchange and regroup kernels in GB/s). ``attaina
 on this GPU (a bf16 MFMA loop from registers and a 1 GiB device copy); every
 GEMM and memory kernel is also reported as a percentage of those
 (``pct_attainable``). Routing kernels report GB/s on their algorithmic bytes
-(fp32 logits and int32 tables).
+(fp32 logits and int32 tables), and as a percentage of the same copy probe
+run at 4 MiB (``pct_copy_4MiB``), the size at which such kernels live.
 """
 from __future__ import annotations
 
@@ -62,6 +63,9 @@ GEMM_KERNELS = {
 }
 MEM_KERNELS = ("permute", "combine", "combine_bwd", "permute_bwd")
 ROUTE_TOKENS = 64  # tokens per workgroup of the route pass (its histograms are [T/64, E] int32)
+# size of the copy the routing kernels are set against: 4 MiB copied (8 MiB of HBM traffic), the order of the
+# 7-13 MB a routing kernel moves on the 32k-token workloads
+ROUTE_COPY_BYTES = 4 << 20
 
 # HBM-side bytes per launch measured with rocprofv3 FETCH_SIZE and WRITE_SIZE
 # passes (each scaled by what the counter reads for a plain 1 GiB device copy:
@@ -239,12 +243,27 @@ def attainable_peaks(dev):
         torch.cuda.synchronize()
         if i >= 3:
             rates.append(2 * nbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
+    # the same copy at the routing kernels' size (a few MB per launch), where
+    # launch and first-access latency, not bandwidth, set the time
+    small = ROUTE_COPY_BYTES
+    small_rates = []
+    for i in range(23):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        moe.moe_peak_copy(src, dst, small)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            small_rates.append(2 * small / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
     del src, dst, out
     torch.cuda.empty_cache()
     rates.sort()
+    small_rates.sort()
     return {"mfma_bf16_tflops": round(best, 1), "copy_GBps": round(rates[len(rates) // 2], 1),
+            "copy_4MiB_GBps": round(small_rates[len(small_rates) // 2], 1),
             "mfma_probe": "v_mfma_f32_32x32x16_bf16 from registers, 2 wavefronts per SIMD x 4 accumulator chains",
-            "copy_probe": f"16-byte non-temporal device copy of {nbytes >> 20} MiB (2x that in HBM traffic)"}
+            "copy_probe": f"16-byte non-temporal device copy of {nbytes >> 20} MiB (2x that in HBM traffic)",
+            "copy_4MiB_probe": f"the same copy of {small >> 20} MiB (median of 20 launches)"}
 
 
 def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
@@ -346,6 +365,7 @@ def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
     peak = PEAK_BF16_TFLOPS if w.dtype == BF16 else PEAK_F32_TFLOPS
     att_tf = attain["mfma_bf16_tflops"] if attain and w.dtype == BF16 else None
     att_bw = attain["copy_GBps"] if attain else None
+    att_bw_small = attain.get("copy_4MiB_GBps") if attain else None
 
     kernels = {}
     for name, (n, ms) in kern.items():
@@ -373,6 +393,8 @@ def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
             entry.update(GBps=round(gbps, 1), pct_peak=round(100 * gbps / PEAK_HBM_GBPS, 2))
             if att_bw:
                 entry["pct_attainable"] = round(100 * gbps / att_bw, 2)
+            if att_bw_small and name.startswith("route_"):
+                entry["pct_copy_4MiB"] = round(100 * gbps / att_bw_small, 2)
         kernels[name] = entry
 
     gemm_names = [n for n in kernels if n.replace("_f32", "") in GEMM_KERNELS]
@@ -425,6 +447,7 @@ def measure(w, args, steps, warmup, attain=None, keep_inputs=False):
         "permute_combine_pct_hbm": round(100 * pc_gbps / PEAK_HBM_GBPS, 2),
         "route_GBps": round(route_gbps, 1),
         "route_pct_hbm": round(100 * route_gbps / PEAK_HBM_GBPS, 2),
+        "route_pct_copy_4MiB": round(100 * route_gbps / att_bw_small, 2) if att_bw_small else None,
         "executed_tflops": round(executed_fl / (ms_per_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
         "ms_per_step_with_kernel_events": round(prof_ms / steps, 4),
@@ -611,7 +634,8 @@ def main():
             r, _ = measure(ow, args, args.other_steps, min(args.warmup, 3), attain)
             keep = ("value", "ms_per_step", "steps", "grouped_gemm_tflops", "grouped_gemm_pct_peak",
                     "grouped_gemm_pct_attainable", "permute_combine_GBps", "permute_combine_pct_hbm",
-                    "permute_combine_pct_attainable", "route_GBps", "route_pct_hbm", "device_memory_GB")
+                    "permute_combine_pct_attainable", "route_GBps", "route_pct_hbm", "route_pct_copy_4MiB",
+                    "device_memory_GB")
             o = {k: r[k] for k in keep if k in r}
             o["T"] = list(ow.microbatches) if ow.micro_T else ow.T
             o["d"], o["E_local"], o["F"] = ow.d, ow.E, ow.F
