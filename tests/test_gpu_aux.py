@@ -75,6 +75,13 @@ CASES = [
     (1000, 256, 16, "normal", 0, 65),
     (3000, 1, 1, "normal", 0, 66),
     (4099, 16, 4, "zipf", 3, 67),
+    # every split of a row over lanes (1, 4 or 8 lanes; 8, 16 or 32 values per lane; rows of single values when E is
+    # not a multiple of 4) and, past 65536 tokens, workgroups that take more than one pass over their tokens
+    (333, 100, 3, "zipf", 4, 72),
+    (129, 129, 5, "normal", 0, 73),
+    (700, 31, 4, "zipf", 2, 74),
+    (130, 5, 2, "normal", 0, 75),
+    (70000, 64, 8, "zipf", 3, 76),
 ]
 
 

@@ -1,16 +1,17 @@
 // MoE auxiliary losses and routing metrics (latency-bound, two launches).
 //
-// Pass 1 (aux_partial_kernel): one wavefront per token, lanes across experts
-// (lane l holds experts l, l+64, l+128, l+192). Per token it forms the full
-// softmax p and lse = log sum exp(logits), adds p into per-lane sums of
-// P_e, lse^2, the entropy -sum p log p (log p taken as logit - lse) and the
-// top probability (= exp(max - lse)), and, if asked, writes the gradient
+// Pass 1 (aux_partial_kernel): each token's row is shared by route_lanes(E)
+// lanes (the routing kernels' split: at most 8 values per lane for E <= 64).
+// Per token it forms the full softmax p and lse = log sum exp(logits), the
+// row maximum and the sums reduced over the token's lanes, adds p into
+// per-lane sums of P_e, lse^2, the entropy -sum p log p (log p taken as
+// logit - lse) and the top probability (= exp(max - lse)), and, if asked,
+// writes the gradient
 //   dlogits[t,i] = p_i (G_i - sum_e p_e G_e) + (2 beta / T) lse p_i,
 //   G_e = alpha E counts[e] / (T^2 k)     (d(alpha L_bal)/dp[t,e])
 // overwriting or adding to dlogits. Each workgroup covers a contiguous run
-// of tokens, its four wavefronts taking every fourth token (four of their
-// tokens in flight at a time); their sums are combined in a fixed order into
-// one partial row [E + 3] per workgroup.
+// of tokens; its sums are combined over token groups and wavefronts in a
+// fixed order into one partial row [E + 3] per workgroup.
 // Pass 2 (aux_finalize_kernel, one workgroup): partial rows summed in eight
 // interleaved chains combined in a fixed order, count statistics, losses and
 // the metrics array.
@@ -24,115 +25,124 @@ namespace moe {
 
 constexpr int kAuxThreads = 256;
 constexpr int kAuxMaxE = 256;
-constexpr int kAuxPerLane = kAuxMaxE / kWave;  // experts per lane
 constexpr int kAuxScalars = 3;                 // entropy, lse^2, top probability
 
-MOE_DEVICE float wave_max(float v) {
+// Sum / maximum over the G lanes of one token (aligned groups of G lanes).
+template <int G>
+MOE_DEVICE float group_sum(float v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+template <int G>
+MOE_DEVICE float group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
+template <int G, int V>
 __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float *__restrict__ logits,
                                                                   const int32_t *__restrict__ counts,
                                                                   float *__restrict__ partial, float *dlogits,
                                                                   int64_t T, int E, int tokens_per_block,
                                                                   float gscale, float zscale, int accumulate) {
+  using Lane = RouteLane<G, V>;
+  constexpr int TPI = kAuxThreads / G;  // tokens of the workgroup per iteration
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
+  const int g = threadIdx.x % G;
+  const bool vec = (E & 3) == 0;
   const int64_t t0 = (int64_t)blockIdx.x * tokens_per_block;
   int64_t t_end = t0 + tokens_per_block;
   if (t_end > T) t_end = T;
-  float G[kAuxPerLane], psum[kAuxPerLane];
+  float Gv[V], psum[V];
 #pragma unroll
-  for (int q = 0; q < kAuxPerLane; ++q) {
-    const int e = lane + kWave * q;
-    G[q] = (dlogits && e < E) ? gscale * (float)counts[e] : 0.f;
-    psum[q] = 0.f;
+  for (int i = 0; i < V; ++i) {
+    const int e = Lane::elem(i, g, vec);
+    Gv[i] = (dlogits && e < E) ? gscale * (float)counts[e] : 0.f;
+    psum[i] = 0.f;
   }
   float ent = 0.f, zz = 0.f, mx = 0.f;
-  // The wavefront's tokens t0 + wv + 4 i are taken TB at a time: loads and
-  // reductions of the TB tokens are independent chains that overlap; the
-  // per-lane sums still take the tokens in order.
-  constexpr int TB = 4;
-  constexpr int WSTEP = kAuxThreads / kWave;
-  for (int64_t tb = t0 + wv; tb < t_end; tb += TB * WSTEP) {
-    float l[TB][kAuxPerLane], m[TB];
+  // a token's G lanes take the same tokens, so the reductions below stay
+  // within lanes that are all active
+  for (int64_t t = t0 + threadIdx.x / G; t < t_end; t += TPI) {
+    const float *row = logits + t * E;
+    float l[V], old[V];
+    Lane::load(row, E, g, vec, l);
+    if (dlogits && accumulate) Lane::load(dlogits + t * E, E, g, vec, old);
+    float m = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int64_t t = tb + u * WSTEP;
-      m[u] = -INFINITY;
+    for (int i = 0; i < V; ++i) {
+      if (Lane::elem(i, g, vec) >= E) l[i] = -INFINITY;  // past the row: exp gives 0
+      m = fmaxf(m, l[i]);
+    }
+    m = group_max<G>(m);
+    float ex[V], sm = 0.f;
 #pragma unroll
-      for (int q = 0; q < kAuxPerLane; ++q) {
-        const int e = lane + kWave * q;
-        l[u][q] = (t < t_end && e < E) ? logits[t * E + e] : -INFINITY;
-        m[u] = fmaxf(m[u], l[u][q]);
+    for (int i = 0; i < V; ++i) {
+      ex[i] = expf(l[i] - m);
+      sm += ex[i];
+    }
+    sm = group_sum<G>(sm);
+    const float inv = 1.f / sm;
+    const float lse = m + logf(sm);
+    float p[V], plogp = 0.f, pg = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      p[i] = ex[i] * inv;
+      if (p[i] > 0.f) plogp += p[i] * (l[i] - lse);
+      pg += p[i] * Gv[i];
+      psum[i] += p[i];
+    }
+    plogp = group_sum<G>(plogp);
+    if (dlogits) {
+      pg = group_sum<G>(pg);
+      float d[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float v = p[i] * (Gv[i] - pg) + zscale * lse * p[i];
+        d[i] = accumulate ? old[i] + v : v;
       }
-    }
+      float *drow = dlogits + t * E;
+      if (vec) {
 #pragma unroll
-    for (int u = 0; u < TB; ++u) m[u] = wave_max(m[u]);
-    float ex[TB][kAuxPerLane], sm[TB];
+        for (int c = 0; c < V / 4; ++c) {
+          const int e = 4 * (g + G * c);
+          if (e < E)
+            *reinterpret_cast<float4 *>(drow + e) = make_float4(d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]);
+        }
+      } else {
 #pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      sm[u] = 0.f;
-#pragma unroll
-      for (int q = 0; q < kAuxPerLane; ++q) {
-        ex[u][q] = expf(l[u][q] - m[u]);  // 0 for -inf and for lanes past E
-        sm[u] += ex[u][q];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TB; ++u) sm[u] = wave_sum(sm[u]);
-    float p[TB][kAuxPerLane], plogp[TB], pg[TB], lse[TB], inv[TB], old[TB][kAuxPerLane];
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int64_t t = tb + u * WSTEP;
-      inv[u] = 1.f / sm[u];
-      lse[u] = m[u] + logf(sm[u]);
-      plogp[u] = 0.f;
-      pg[u] = 0.f;
-#pragma unroll
-      for (int q = 0; q < kAuxPerLane; ++q) {
-        const int e = lane + kWave * q;
-        p[u][q] = ex[u][q] * inv[u];
-        if (p[u][q] > 0.f) plogp[u] += p[u][q] * (l[u][q] - lse[u]);
-        pg[u] += p[u][q] * G[q];
-        old[u][q] = (dlogits && accumulate && t < t_end && e < E) ? dlogits[t * E + e] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      plogp[u] = wave_sum(plogp[u]);
-      if (dlogits) pg[u] = wave_sum(pg[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int64_t t = tb + u * WSTEP;
-      if (t >= t_end) break;  // uniform: the rest of the batch is past the run
-#pragma unroll
-      for (int q = 0; q < kAuxPerLane; ++q) psum[q] += p[u][q];
-      ent -= plogp[u];
-      zz += lse[u] * lse[u];
-      mx += inv[u];  // the top probability is exp(m - lse) = 1 / s
-      if (dlogits) {
-        float *drow = dlogits + t * E;
-#pragma unroll
-        for (int q = 0; q < kAuxPerLane; ++q) {
-          const int e = lane + kWave * q;
-          if (e < E) {
-            const float v = p[u][q] * (G[q] - pg[u]) + zscale * lse[u] * p[u][q];
-            drow[e] = accumulate ? old[u][q] + v : v;
-          }
+        for (int i = 0; i < V; ++i) {
+          const int e = g + G * i;
+          if (e < E) drow[e] = d[i];
         }
       }
     }
+    if (g == 0) {  // the token's scalars once
+      ent -= plogp;
+      zz += lse * lse;
+      mx += inv;  // the top probability is exp(m - lse) = 1 / s
+    }
   }
+  // P_e: lanes g of every token group hold the same experts; add over the
+  // wavefront's token groups, then over the wavefronts, in a fixed order
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+#pragma unroll
+    for (int o = G; o < kWave; o <<= 1) psum[i] += __shfl_xor(psum[i], o, kWave);
+  ent = wave_sum(ent);
+  zz = wave_sum(zz);
+  mx = wave_sum(mx);
   __shared__ float sp[kAuxThreads / kWave][kAuxMaxE];
   __shared__ float ss[kAuxThreads / kWave][kAuxScalars];
+  if (lane < G) {
 #pragma unroll
-  for (int q = 0; q < kAuxPerLane; ++q) {
-    const int e = lane + kWave * q;
-    if (e < E) sp[wv][e] = psum[q];
+    for (int i = 0; i < V; ++i) {
+      const int e = Lane::elem(i, g, vec);
+      if (e < E) sp[wv][e] = psum[i];
+    }
   }
   if (lane == 0) {
     ss[wv][0] = ent;
@@ -177,22 +187,36 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(const float *
                                                                    const int32_t *__restrict__ counts, int64_t T,
                                                                    int E, int k, float *losses, float *metrics) {
   __shared__ float red[kAuxThreads];
-  const int e = threadIdx.x;  // E <= 256: one expert per thread
+  // column sums of the partial rows: eight interleaved chains per column
+  // (rows r mod 8, ascending), combined in a fixed order; thread t takes
+  // chain t / 32 of column t % 32 of each pass over 32 columns, so that a
+  // row's columns are read together
+  constexpr int kChains = 8;
+  constexpr int kCols = kAuxThreads / kChains;
+  __shared__ float chain[kChains][kAuxMaxE + kAuxScalars];
   const int ld = E + kAuxScalars;
+  for (int c0 = 0; c0 < ld; c0 += kCols) {
+    const int col = c0 + (int)threadIdx.x % kCols;
+    const int r = (int)threadIdx.x / kCols;
+    if (col < ld) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int b = r; b < nblk; b += kChains) acc += partial[(int64_t)b * ld + col];
+      chain[r][col] = acc;
+    }
+  }
+  __syncthreads();
+  auto column = [&](int col) {
+    return ((chain[0][col] + chain[1][col]) + (chain[2][col] + chain[3][col])) +
+           ((chain[4][col] + chain[5][col]) + (chain[6][col] + chain[7][col]));
+  };
+  const int e = threadIdx.x;  // E <= 256: one expert per thread
   const float Tf = (float)T;
   const float rows = (float)((double)T * k);
   const float mean = (float)((double)T * k / E);
   float fP = 0.f, dev2 = 0.f, cmax = 0.f, empty = 0.f;
   if (e < E) {
-    // eight interleaved partial sums (rows b = r mod 8), added in a fixed order
-    float P8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int b = 0;
-    for (; b + 8 <= nblk; b += 8)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) P8[r] += partial[(int64_t)(b + r) * ld + e];
-    for (int r = 0; b + r < nblk; ++r) P8[r] += partial[(int64_t)(b + r) * ld + e];
-    float P = ((P8[0] + P8[1]) + (P8[2] + P8[3])) + ((P8[4] + P8[5]) + (P8[6] + P8[7]));
-    P /= Tf;
+    const float P = column(e) / Tf;
     const float c = (float)counts[e];
     const float f = c / rows;
     fP = f * P;
@@ -204,16 +228,7 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(const float *
       metrics[MOE_METRIC_SCALARS + E + e] = P;
     }
   }
-  float sc = 0.f;
-  if (e < kAuxScalars) {
-    float S8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int b = 0;
-    for (; b + 8 <= nblk; b += 8)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) S8[r] += partial[(int64_t)(b + r) * ld + E + e];
-    for (int r = 0; b + r < nblk; ++r) S8[r] += partial[(int64_t)(b + r) * ld + E + e];
-    sc = ((S8[0] + S8[1]) + (S8[2] + S8[3])) + ((S8[4] + S8[5]) + (S8[6] + S8[7]));
-  }
+  const float sc = e < kAuxScalars ? column(E + e) : 0.f;
   const float sum_fP = block_sum_256(fP, red);
   const float sum_dev2 = block_sum_256(dev2, red);
   const float sum_empty = block_sum_256(empty, red);
@@ -247,6 +262,13 @@ __global__ __launch_bounds__(kAuxThreads) void aux_empty_kernel(float *losses, f
       metrics[q] = q == MOE_METRIC_EMPTY_EXPERTS ? (float)E : 0.f;
 }
 
+template <int G, int V>
+static void aux_partial_t(const float *logits, const int32_t *counts, float *partial, float *dlogits, int64_t T,
+                          int E, int tpb, int nblk, float gscale, float zscale, int acc, hipStream_t s) {
+  aux_partial_kernel<G, V><<<nblk, kAuxThreads, 0, s>>>(logits, counts, partial, dlogits, T, E, tpb, gscale, zscale,
+                                                        acc);
+}
+
 hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *losses, float *metrics, float *dlogits,
                            float *partial, int64_t T, int E, int k, float alpha, float beta, bool accumulate,
                            hipStream_t s) {
@@ -262,8 +284,15 @@ hipError_t launch_aux_loss(const float *logits, const int32_t *counts, float *lo
   const float zscale = (float)(2.0 * beta / (double)T);
   {
     LaunchScope scope("aux_partial", s);
-    aux_partial_kernel<<<nblk, kAuxThreads, 0, s>>>(logits, counts, partial, dlogits, T, E, tpb, gscale, zscale,
-                                                     accumulate ? 1 : 0);
+    const int acc = accumulate ? 1 : 0;
+    switch (route_lanes(E) * route_lane_values(E)) {  // (G, V): (1, 8) (2, 8) (4, 8) (8, 8) (8, 16) (8, 32)
+      case 8: aux_partial_t<1, 8>(logits, counts, partial, dlogits, T, E, tpb, nblk, gscale, zscale, acc, s); break;
+      case 16: aux_partial_t<2, 8>(logits, counts, partial, dlogits, T, E, tpb, nblk, gscale, zscale, acc, s); break;
+      case 32: aux_partial_t<4, 8>(logits, counts, partial, dlogits, T, E, tpb, nblk, gscale, zscale, acc, s); break;
+      case 64: aux_partial_t<8, 8>(logits, counts, partial, dlogits, T, E, tpb, nblk, gscale, zscale, acc, s); break;
+      case 128: aux_partial_t<8, 16>(logits, counts, partial, dlogits, T, E, tpb, nblk, gscale, zscale, acc, s); break;
+      default: aux_partial_t<8, 32>(logits, counts, partial, dlogits, T, E, tpb, nblk, gscale, zscale, acc, s); break;
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || (!losses && !metrics)) return err;

@@ -39,12 +39,13 @@ struct WorkspaceLayout {
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tokens per workgroup of the auxiliary-loss pass: at least 256, at most
-// kAuxMaxBlocks workgroups, a multiple of 4 (one token per wavefront in turn).
+// Tokens per workgroup of the auxiliary-loss pass: at least kAuxMinTokens
+// (512 workgroups at 32k tokens), at most kAuxMaxBlocks workgroups.
+constexpr int kAuxMinTokens = 64;
 inline int aux_tokens_per_block(int64_t T) {
   int64_t tpb = ceil_div(T, kAuxMaxBlocks);
-  if (tpb < 256) tpb = 256;
-  return (int)((tpb + 3) / 4 * 4);
+  if (tpb < kAuxMinTokens) tpb = kAuxMinTokens;
+  return (int)tpb;
 }
 
 // Validates the shape alone. On failure writes a message to *why.
