@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "route_lane.h"
 
 namespace moe {
 

@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "route_lane.h"
 
 namespace moe {
 
