@@ -125,6 +125,8 @@ def shape(T=64, d=64, E=4, k=2, F=128, dtype=L.MOE_DTYPE_BF16, flags=0):
     (dict(T=2 ** 24, E=8, k=1), L.MOE_ERR_UNSUPPORTED),  # 256 threads per token: 2^32 threads
     (dict(T=2 ** 20, d=32768, E=8, k=1), L.MOE_ERR_UNSUPPORTED),  # T*d/8 = 2^32 chunks
     (dict(T=2 ** 19, d=32768, E=256, k=1, F=32768), L.MOE_ERR_UNSUPPORTED),  # weight-gradient grid
+    # fp32 grouped GEMM: 16-wide tiles over 2^25 rows pass 2^32 threads
+    (dict(T=2 ** 24 - 1, E=8, k=2, F=64, dtype=L.MOE_DTYPE_F32), L.MOE_ERR_UNSUPPORTED),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(moe.MoeError) as ei:
@@ -136,6 +138,8 @@ def test_large_shapes_within_the_launch_bounds_are_accepted():
     # just inside each bound: 2^24 - 1 tokens, T*d/8 just under 2^32
     moe.moe_workspace_size(shape(T=2 ** 24 - 1, E=8, k=1))
     moe.moe_workspace_size(shape(T=2 ** 20 - 1, d=32768, E=8, k=1))
+    # the routing test at the largest token count: bf16, top-2
+    moe.moe_workspace_size(shape(T=2 ** 24 - 1, E=8, k=2, F=64))
 
 
 def test_empty_microbatch_is_a_noop_with_nulls():
