@@ -74,16 +74,16 @@ ROUTE_COPY_BYTES = 4 << 20
 TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h")
 TRAFFIC = {
-    "sources_sha256": "82735855132b2045d9600be8d6bd55704443641731de0e30db4a1e5d5a0cf900",
+    "sources_sha256": "8150f8b1e641fb9543cc4f2d1a60efcf6a939a092f34903ebc45c326c32397fb",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.764 + 2.064) * 2 ** 30,
-        "gg_down_fwd": (2.411 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.449 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (5.728 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (5.071 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.668 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.918 + 2.064) * 2 ** 30,
+        "gg_down_fwd": (2.393 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.501 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (6.402 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (4.929 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.695 + 0.645) * 2 ** 30,
     },
 }
 

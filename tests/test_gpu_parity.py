@@ -182,6 +182,11 @@ SMALL_CASES = [
     ("f32_d1088_cbwd_token_tail", small_workload(7, 1088, 3, 2, 64, F32, "normal", seed=42), False),
     ("bf16_d4160_cbwd_row_tail", small_workload(13, 4160, 5, 3, 64, BF16, "normal", seed=43), False),
     ("f32_d2048_cbwd_row", small_workload(11, 2048, 4, 1, 64, F32, "zipf", seed=44), False),
+    # the down weight gradient's edge tiles (F an odd multiple of 128, d a multiple of 512: the last 128 columns
+    # of dW_down as 512 x 128 tiles): beside 256 x 256 tiles with empty experts, and alone (F = 128, no 256-wide
+    # column tile at all)
+    ("bf16_wgrad_edge_tiles", small_workload(900, 1024, 8, 2, 384, BF16, "zipf", seed=45, n_empty=2), False),
+    ("bf16_wgrad_edge_only", small_workload(333, 512, 5, 3, 128, BF16, "normal", seed=46), False),
 ]
 
 
