@@ -187,6 +187,10 @@ SMALL_CASES = [
     # column tile at all)
     ("bf16_wgrad_edge_tiles", small_workload(900, 1024, 8, 2, 384, BF16, "zipf", seed=45, n_empty=2), False),
     ("bf16_wgrad_edge_only", small_workload(333, 512, 5, 3, 128, BF16, "normal", seed=46), False),
+    # F an odd multiple of 128 with experts of many row tiles: the down dgrad's half-empty last column tile
+    # (columns past F clamped on load, never stored) on Zipf experts of 11, 6 and 8 row tiles and an empty
+    # one, beside full 256 x 256 tiles, in every product
+    ("bf16_F640_half_column_tiles", small_workload(3000, 256, 4, 2, 640, BF16, "zipf", seed=47, n_empty=1), False),
 ]
 
 
