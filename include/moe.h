@@ -470,8 +470,10 @@ const char *moe_last_error(void);
  * kernel the library launches is bracketed by two events recorded on the
  * launch stream; moe_profiler_read() waits for them and returns, per kernel
  * name, the number of launches and the summed elapsed milliseconds since the
- * last moe_profiler_reset(). Host-side state, not thread-safe; meant for a
- * single measuring thread. Disabled by default.
+ * last moe_profiler_reset(). Process-wide host-side state guarded by a
+ * mutex: launches from several threads are timed together, and a read blocks
+ * until the events of its entry have completed. Meant for measurement;
+ * disabled by default.
  */
 moe_status moe_profiler_enable(int on);
 moe_status moe_profiler_reset(void);

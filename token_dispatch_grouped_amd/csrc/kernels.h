@@ -29,13 +29,14 @@ inline int64_t router_chunks(int64_t T) {
 }
 
 // Per-kernel timing hook (profiler in moe_abi.cpp). Brackets a launch with
-// events when enabled.
+// events when enabled; the pair joins the timer's records once both are
+// recorded.
 struct LaunchScope {
   LaunchScope(const char *name, hipStream_t s);
   ~LaunchScope();
   const char *name_;
   hipStream_t stream_;
-  int slot_;
+  hipEvent_t start_, end_;
 };
 
 // ----- routing -----

@@ -12,7 +12,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -57,8 +59,11 @@ struct ProfEntry {
   double ms = 0.0;
 };
 
+// Process-wide; every member but `on` is used under `mu`, so launches on
+// several threads (and reads beside them) may be timed together.
 struct Profiler {
-  bool on = false;
+  std::atomic<bool> on{false};
+  std::mutex mu;
   std::vector<ProfEntry> entries;
   std::vector<hipEvent_t> pool;
 
@@ -95,18 +100,30 @@ struct Profiler {
 
 static Profiler g_prof;
 
-LaunchScope::LaunchScope(const char *name, hipStream_t s) : name_(name), stream_(s), slot_(-1) {
-  if (!g_prof.on) return;
-  hipEvent_t a = g_prof.take(), b = g_prof.take();
-  if (!a || !b) return;
-  slot_ = g_prof.slot(name);
-  g_prof.entries[slot_].live.push_back({a, b});
-  (void)hipEventRecord(a, s);
+LaunchScope::LaunchScope(const char *name, hipStream_t s) : name_(name), stream_(s), start_(nullptr), end_(nullptr) {
+  if (!g_prof.on.load(std::memory_order_relaxed)) return;
+  {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    start_ = g_prof.take();
+    end_ = g_prof.take();
+  }
+  if (!start_ || !end_) {  // no events: this launch goes untimed
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    if (start_) g_prof.pool.push_back(start_);
+    if (end_) g_prof.pool.push_back(end_);
+    start_ = end_ = nullptr;
+    return;
+  }
+  (void)hipEventRecord(start_, s);
 }
 
+// The pair is handed to the timer only now that both events are recorded,
+// so a read never waits on an event that has not been recorded yet.
 LaunchScope::~LaunchScope() {
-  if (slot_ < 0) return;
-  (void)hipEventRecord(g_prof.entries[slot_].live.back().second, stream_);
+  if (!end_) return;
+  (void)hipEventRecord(end_, stream_);
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  g_prof.entries[g_prof.slot(name_)].live.push_back({start_, end_});
 }
 
 }  // namespace moe
@@ -656,19 +673,24 @@ moe_status moe_peak_copy(const void *src, void *dst, int64_t bytes, moe_stream_t
 }
 
 moe_status moe_profiler_enable(int on) {
-  g_prof.on = on != 0;
+  g_prof.on.store(on != 0);
   return MOE_OK;
 }
 
 moe_status moe_profiler_reset(void) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
   for (size_t i = 0; i < g_prof.entries.size(); ++i) g_prof.drain((int)i);
   g_prof.entries.clear();
   return MOE_OK;
 }
 
-int moe_profiler_count(void) { return (int)g_prof.entries.size(); }
+int moe_profiler_count(void) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  return (int)g_prof.entries.size();
+}
 
 moe_status moe_profiler_read(int i, const char **name, int64_t *launches, double *total_ms) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
   if (i < 0 || i >= (int)g_prof.entries.size()) return report(MOE_ERR_INVALID_ARGUMENT, "profiler index out of range");
   g_prof.drain(i);
   const ProfEntry &en = g_prof.entries[i];
