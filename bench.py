@@ -70,20 +70,22 @@ ROUTE_COPY_BYTES = 4 << 20
 # HBM-side bytes per launch measured with rocprofv3 FETCH_SIZE and WRITE_SIZE
 # passes (each scaled by what the counter reads for a plain 1 GiB device copy:
 # x2.0 and x1.0), on the ep_share_32k workload. Valid only for the GEMM
-# sources they were taken on: any change to those files reports null.
-TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_common.h",
-                   "token_dispatch_grouped_amd/csrc/common.h")
+# sources and build options they were taken on: any change to those files
+# reports null.
+TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispatch_grouped_amd/csrc/gemm_bf16_ilp.hip",
+                   "token_dispatch_grouped_amd/csrc/gemm_bf16_kernel.h", "token_dispatch_grouped_amd/csrc/gemm_common.h",
+                   "token_dispatch_grouped_amd/csrc/common.h", "token_dispatch_grouped_amd/build.py")
 TRAFFIC = {
-    "sources_sha256": "8150f8b1e641fb9543cc4f2d1a60efcf6a939a092f34903ebc45c326c32397fb",
+    "sources_sha256": "85deae1e66f19db5344a2f7521b4a52b840c60d59ee70d2bb39214ccfd9f882f",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30
-        "gg_gateup_fwd": (6.918 + 2.064) * 2 ** 30,
-        "gg_down_fwd": (2.393 + 1.000) * 2 ** 30,
-        "gg_down_dgrad": (4.501 + 1.375) * 2 ** 30,
-        "gg_down_wgrad": (6.402 + 0.322) * 2 ** 30,
-        "gg_gateup_dgrad": (4.929 + 1.000) * 2 ** 30,
-        "gg_gateup_wgrad": (10.695 + 0.645) * 2 ** 30,
+        "gg_gateup_fwd": (6.646 + 2.062) * 2 ** 30,
+        "gg_down_fwd": (2.419 + 1.000) * 2 ** 30,
+        "gg_down_dgrad": (4.589 + 1.375) * 2 ** 30,
+        "gg_down_wgrad": (6.364 + 0.322) * 2 ** 30,
+        "gg_gateup_dgrad": (5.061 + 1.000) * 2 ** 30,
+        "gg_gateup_wgrad": (10.677 + 0.645) * 2 ** 30,
     },
 }
 
