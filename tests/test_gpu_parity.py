@@ -221,8 +221,44 @@ def _random_cases(n=14, seed=2024):
 RANDOM_CASES = _random_cases()
 
 
+def _random_wide_cases(n=30, seed=777):
+    """Seeded random shapes over a wider part of the matrix than _random_cases: T from 0 to 4096, d and F up to
+    1024, E up to 256 (odd counts among them), k up to 16, both dtypes, renorm, Zipf tails with empty experts;
+    each case's oracle work is bounded (18*T*k*d*F <= 4e10 FLOP)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = BF16 if rng.random() < 0.8 else F32
+        E = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 32, 33, 64, 100, 128, 255, 256]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        d = 64 * int(rng.integers(1, 17))
+        F = 64 * int(rng.integers(1, 17))
+        T = int(rng.integers(0, 4097))
+        if 18.0 * max(T, 1) * k * d * F > 4e10:
+            continue
+        routing = "zipf" if rng.random() < 0.6 else "normal"
+        n_empty = int(rng.integers(0, E - k + 1)) if routing == "zipf" and E > k else 0
+        renorm = bool(rng.random() < 0.3)
+        s = int(rng.integers(100, 100000))
+        name = f"wide{len(cases)}_T{T}_d{d}_E{E}_k{k}_F{F}_{dtype}_{routing}{n_empty}{'_renorm' if renorm else ''}"
+        cases.append((name, small_workload(T, d, E, k, F, dtype, routing, seed=s, n_empty=n_empty), renorm))
+    return cases
+
+
+RANDOM_WIDE_CASES = _random_wide_cases()
+
+
 @pytest.mark.parametrize("name,w,renorm", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
 def test_layer_random_shapes(name, w, renorm):
+    print(f"[parity] {name}", flush=True)
+    inp = make_inputs(w)
+    gres, gacc = gpu_run(w, inp, renorm)
+    ores, oacc = oracle_run(w, inp, renorm)
+    compare(w, gres, gacc, ores, oacc, renorm)
+
+
+@pytest.mark.parametrize("name,w,renorm", RANDOM_WIDE_CASES, ids=[c[0] for c in RANDOM_WIDE_CASES])
+def test_layer_random_wide_shapes(name, w, renorm):
     print(f"[parity] {name}", flush=True)
     inp = make_inputs(w)
     gres, gacc = gpu_run(w, inp, renorm)
