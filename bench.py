@@ -76,7 +76,7 @@ TRAFFIC_SOURCES = ("token_dispatch_grouped_amd/csrc/gemm_bf16.hip", "token_dispa
                    "token_dispatch_grouped_amd/csrc/gemm_bf16_kernel.h", "token_dispatch_grouped_amd/csrc/gemm_common.h",
                    "token_dispatch_grouped_amd/csrc/common.h", "token_dispatch_grouped_amd/build.py")
 TRAFFIC = {
-    "sources_sha256": "85deae1e66f19db5344a2f7521b4a52b840c60d59ee70d2bb39214ccfd9f882f",
+    "sources_sha256": "5cb16b5d5c047803b0bcdf39d692ce7317c4aa2be384891d536bff0bd5b661b7",
     "workload": "ep_share_32k",
     "bytes_per_launch": {
         # read GiB + write GiB, x 2^30

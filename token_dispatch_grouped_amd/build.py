@@ -24,7 +24,7 @@ SOURCES = ["moe_abi.cpp", "validate.cpp", "route.hip", "dispatch.hip", "gemm_bf1
            "gemm_f32.hip", "optim.hip", "aux.hip", "peak.hip", "ep.hip"]
 # Per-source compiler options: the gate/up forward and weight-gradient GEMM
 # kernels (gemm_bf16_ilp.hip) are scheduled for instruction-level parallelism,
-# which makes them 1.6-1.8% faster and the dgrad kernels slower (those are in
+# which makes them 0.5-1.8% faster and the dgrad kernels slower (those are in
 # gemm_bf16.hip, default scheduler).
 SOURCE_FLAGS = {"gemm_bf16_ilp.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
 ARCH = "gfx950"

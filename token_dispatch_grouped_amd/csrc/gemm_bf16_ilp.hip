@@ -1,9 +1,9 @@
 // The gate/up forward (SwiGLU epilogue) and the weight-gradient kernels of
 // the grouped expert GEMMs, instantiated here so that this file alone is
 // compiled with the max-ILP machine scheduler (build.py): with it those
-// kernels run 1.6-1.8% faster on the 32k-token workload, while the dgrad
+// kernels run 0.5-1.8% faster on the 32k-token workload, while the dgrad
 // products run 2-3% slower, so they stay with the default scheduler in
-// gemm_bf16.hip (same-box A/B runs).
+// gemm_bf16.hip (same-box A/B runs on three boxes).
 #include "gemm_bf16_kernel.h"
 
 namespace moe {
