@@ -10,10 +10,12 @@ over the experts of each token.
     expert's rows of h, a, y, dy, dh and dx_perm; every expert's dw_gu and
     dw_down (the heaviest, with ~32k rows, included; empty experts exactly
     zero); out, dx, dtopk_w and dlogits for every token.
-  * large_share_zipf / large_share_uniform (d=4096, E=64, F=1536): the tables
-    bit for bit, sampled dispatched rows bit for bit, sampled tokens' outputs
-    and token-side gradients, and the full weight gradients of the heaviest,
-    a median and the lightest expert.
+  * large_share_uniform (d=4096, E=64, F=1536) is compared in full the same
+    way (every expert's rows and weight gradients, every token).
+  * large_share_zipf / large_share_uniform: the tables bit for bit, sampled
+    dispatched rows bit for bit, sampled tokens' outputs and token-side
+    gradients, and the full weight gradients of the heaviest, a median and the
+    lightest expert.
   * microbatches_32k (T = 16384, 7001, 0, 32768 on one set of buffers): each
     microbatch's tables bit for bit and sampled tokens, then the accumulated
     weight gradients of the heaviest and the lightest expert that is live in
@@ -87,10 +89,12 @@ def _check_dw(e, o, dw_gu, dw_dn, tol):
     assert_close(f"dw_down[{e}]", to_host64(dw_dn[e]), o["dw_down"], tol)
 
 
-def test_fullsize_every_expert_ep_share_32k():
-    """The bench workload compared in full, one expert at a time."""
+@pytest.mark.parametrize("name", ["ep_share_32k", "large_share_uniform"])
+def test_fullsize_every_expert(name):
+    """The bench workload, and the d = 4096 share with uniform routing,
+    compared in full, one expert at a time."""
     import torch
-    w = WORKLOADS["ep_share_32k"]
+    w = WORKLOADS[name]
     print(f"[fullsize] every expert {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
     inp = make_inputs(w)
     mb, W = inp["micro"][0], inp["weights"]
