@@ -390,6 +390,8 @@ def test_workspace_reuse_across_sizes():
 
 RECOMPUTE_CASES = [c for c in SMALL_CASES if c[0] in (
     "tiny_f32_router", "bf16_ragged_tiles_zipf", "bf16_renorm_k8", "f32_zipf", "bf16_E256_k16", "bf16_single_expert")]
+# and the first wide random shapes (both dtypes, renorm, E up to 255, d up to 1024)
+RECOMPUTE_CASES += RANDOM_WIDE_CASES[:8]
 
 
 def _assert_bitwise(a_res, a_acc, b_res, b_acc):
